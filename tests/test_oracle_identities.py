@@ -1,0 +1,206 @@
+"""Exact identities and special cases that pin the oracle.
+
+* Re-association (FAVOR+ blog page, section 核心机制：FAVOR+): the
+  linear-order result equals the explicit D^-1 A V form with the same
+  features, to float64 rounding.
+* Causal prefix sum (same section, causal variant): equals the
+  lower-triangular (diagonal included) masked form.
+* Special cases with closed forms: a single token, constant values,
+  linearity, permutation symmetry, equal keys, the zero feature matrix
+  (which reduces the trig map to a key-norm-weighted mean), ReLU convexity.
+"""
+import numpy as np
+import pytest
+
+from linear_kernelized_attention_amd import inputs as I
+from oracle import favor_oracle as O
+
+
+def _case(B=2, H=2, L=37, d=8, m=16, seed=0, dtype="f32"):
+    a = I.attention_inputs(B, H, L, d, dtype, seed=seed)
+    dr = I.omega_draws(m, d, seed=seed)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, m)
+    return a.q64, a.k64, a.v64, W
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_equals_quadratic(kind, causal):
+    Q, K, V, W = _case()
+    lin = O.favor_attention(Q, K, V, W, kind, causal)
+    quad = O.favor_quadratic(Q, K, V, W, kind, causal)
+    assert _rel(lin, quad) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+def test_causal_blocking_irrelevant(kind):
+    # the carried state across blocks gives the same prefix for any block size
+    Q, K, V, W = _case(B=1, H=1, L=300, d=8, m=16, seed=3)
+    a = O.favor_attention(Q, K, V, W, kind, True)
+    b = O._causal_head(Q[0, 0], K[0, 0], V[0, 0], W, kind, block=7)
+    assert _rel(a[0, 0], b) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_forms(kind, causal):
+    Q, K, V, W = _case(B=1, H=2, L=200, d=8, m=16, seed=4)
+    rows = np.array([199, 0, 5, 6, 100, 1])
+    full = O.favor_attention(Q, K, V, W, kind, causal)
+    r1 = O.favor_rows(Q, K, V, W, kind, causal, rows)
+    r2 = O.favor_quadratic_rows(Q, K, V, W, kind, causal, rows)
+    assert _rel(r1, full[..., rows, :]) <= 1e-12
+    assert _rel(r2, full[..., rows, :]) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token(kind, causal):
+    Q, K, V, W = _case(L=1)
+    out = O.favor_attention(Q, K, V, W, kind, causal)
+    if kind == "relu":
+        # a query with phi(q).phi(k) == 0 gives 0/0 by design; this seed
+        # has positive overlap for every head.
+        assert np.all(np.isfinite(out))
+    assert np.allclose(out, V, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+def test_causal_first_and_last_rows(kind):
+    Q, K, V, W = _case(L=50)
+    c = O.favor_attention(Q, K, V, W, kind, True)
+    b = O.favor_attention(Q, K, V, W, kind, False)
+    assert np.allclose(c[..., 0, :], V[..., 0, :], rtol=1e-12, atol=1e-15)
+    assert np.allclose(c[..., -1, :], b[..., -1, :], rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values(kind, causal):
+    Q, K, V, W = _case()
+    row = np.linspace(-1, 2, V.shape[-1])
+    Vc = np.broadcast_to(row, V.shape)
+    out = O.favor_attention(Q, K, Vc, W, kind, causal)
+    assert np.allclose(out, Vc, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_in_values(kind, causal):
+    Q, K, V, W = _case()
+    V2 = np.random.default_rng(1).standard_normal(V.shape)
+    f = lambda X: O.favor_attention(Q, K, X, W, kind, causal)
+    assert _rel(f(2.5 * V - 0.75 * V2), 2.5 * f(V) - 0.75 * f(V2)) <= 1e-11
+
+
+@pytest.mark.parametrize("kind", O.KINDS)
+def test_permutation_symmetry(kind):
+    Q, K, V, W = _case(L=41)
+    p = np.random.default_rng(2).permutation(41)
+    base = O.favor_attention(Q, K, V, W, kind, False)
+    kv = O.favor_attention(Q, K[..., p, :], V[..., p, :], W, kind, False)
+    qq = O.favor_attention(Q[..., p, :], K, V, W, kind, False)
+    assert _rel(kv, base) <= 1e-12
+    assert _rel(qq, base[..., p, :]) <= 1e-12
+
+
+@pytest.mark.filterwarnings("ignore:invalid value")
+@pytest.mark.parametrize("kind", O.KINDS)
+def test_equal_keys_give_means(kind):
+    Q, K, V, W = _case(L=30)
+    Ke = np.broadcast_to(K[..., :1, :], K.shape)
+    b = O.favor_attention(Q, Ke, V, W, kind, False)
+    c = O.favor_attention(Q, Ke, V, W, kind, True)
+    # ReLU: a query whose features do not overlap the key's gets 0/0
+    # (no epsilon in the denominator); those rows are NaN and skipped.
+    ok = np.isfinite(b).all(axis=-1)
+    assert ok.mean() > 0.8 and np.array_equal(ok, np.isfinite(c).all(axis=-1))
+    mean = np.broadcast_to(V.mean(axis=-2, keepdims=True), V.shape)
+    assert np.allclose(b[ok], mean[ok], rtol=1e-11, atol=1e-13)
+    run = np.cumsum(V, axis=-2) / np.arange(1, 31)[:, None]
+    assert np.allclose(c[ok], run[ok], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_features_key_norm_weighting(causal):
+    # With Omega = 0 the trig features are exp(|x~|^2/2) m^-1/2 [0, 1], so
+    # phi(q).phi(k) = exp(|q~|^2/2 + |k~|^2/2): the query factor cancels
+    # and out_i is the mean of v_j weighted by exp(|k_j|^2 / (2 sqrt(d))).
+    Q, K, V, W = _case(d=16, m=16)
+    Wz = np.zeros_like(W)
+    out = O.favor_attention(Q, K, V, Wz, "trig", causal)
+    w = np.exp(np.sum(K * K, axis=-1) / (2 * np.sqrt(16)))
+    if causal:
+        num = np.cumsum(w[..., None] * V, axis=-2)
+        den = np.cumsum(w, axis=-1)[..., None]
+    else:
+        num = np.sum(w[..., None] * V, axis=-2, keepdims=True)
+        den = np.sum(w, axis=-1)[..., None, None]
+    assert np.allclose(out, np.broadcast_to(num / den, out.shape), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_relu_rows_convex_combinations(causal):
+    Q, K, V, W = _case(L=60, seed=5)
+    out = O.favor_attention(Q, K, V, W, "relu", causal)
+    phq = O.feature_map(Q, W, "relu")
+    phk = O.feature_map(K, W, "relu")
+    assert np.all(phq @ np.swapaxes(phk, -1, -2) >= 0)
+    for i in range(60):
+        hi = (V[..., : i + 1, :] if causal else V).max(axis=-2)
+        lo = (V[..., : i + 1, :] if causal else V).min(axis=-2)
+        assert np.all(out[..., i, :] <= hi + 1e-12) and np.all(out[..., i, :] >= lo - 1e-12)
+
+
+def test_feature_widths():
+    Q, K, V, W = _case(m=16)
+    assert O.feature_map(Q, W, "trig").shape[-1] == 32
+    assert O.feature_map(Q, W, "relu").shape[-1] == 16
+
+
+def test_relu_scale_invariance():
+    # max(0, .) is positively homogeneous: scaling Q or K by c > 0
+    # leaves the output unchanged.
+    Q, K, V, W = _case()
+    a = O.favor_attention(Q, K, V, W, "relu")
+    b = O.favor_attention(3.0 * Q, 0.25 * K, V, W, "relu")
+    assert _rel(b, a) <= 1e-12
+
+
+def test_softmax_matches_torch_sdpa():
+    import torch
+    Q, K, V, _ = _case(L=19, d=8)
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), is_causal=causal).numpy()
+        assert _rel(O.softmax_attention(Q, K, V, causal), ref) <= 1e-12
+
+
+def test_block_reduces_to_attention():
+    # One head of width 64 with identity projections: the block is
+    # FAVOR attention of the embedded tokens with themselves.
+    rng = np.random.default_rng(0)
+    ids = rng.integers(0, 26, size=(1, 40))
+    E = rng.standard_normal((26, 64)) * 0.5
+    eye = np.eye(64)
+    dr = I.omega_draws(64, 64, seed=0)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, 64)
+    y = O.performer_block(ids, E, eye, eye, eye, eye, W, heads=1, kind="relu")
+    X = E[ids][:, None]
+    ref = O.favor_attention(X, X, X, W, "relu")[:, 0]
+    assert _rel(y, ref) <= 1e-12
+
+
+def test_block_same_token_same_row():
+    b = I.block_inputs(B=1, L=128, E=128, H=2, seed=0)
+    dr = I.omega_draws(64, 64, seed=0)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, 64)
+    y = O.performer_block(b.ids, b.embed64, b.wq64, b.wk64, b.wv64, b.wo64, W, heads=2)
+    ids = b.ids[0]
+    for t in np.unique(ids):
+        rows = y[0, ids == t]
+        assert np.allclose(rows, rows[:1], rtol=1e-12, atol=1e-15)
