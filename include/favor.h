@@ -1,0 +1,175 @@
+/*
+ * favor.h -- C ABI of the MI355X (gfx950) FAVOR attention library.
+ *
+ * FAVOR replaces softmax attention D^-1 A V, A = exp(Q K^T / sqrt(d)), by
+ * the factorised kernel phi(q)^T phi(k) built from random features, and
+ * re-associates the products so that no L x L matrix is formed: the keys
+ * and values are first contracted into S = phi(K)^T V and z = phi(K)^T 1,
+ * which are then left-multiplied by phi(Q) and normalised row by row.
+ * The causal variant uses inclusive prefix sums of phi(k_j) v_j^T.
+ * (FAVOR+ blog page "用随机特征“骗”过 softmax，Transformer 注意力也能跑成
+ * 线性？", section 核心机制：FAVOR+; "Masked Language Modeling for Proteins
+ * via Linearly Scalable Long-Context Transformers" summary pages, sections
+ * Methodology / 方法论 and 核心创新.)
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are device memory owned by the caller, except
+ *    where an argument is documented as host memory.  The library never
+ *    allocates or frees device memory and keeps no mutable global state;
+ *    concurrent calls on different streams are safe.
+ *  - Tensors are dense row-major.  Attention tensors are [B, H, L, d] with
+ *    d fastest; Omega is [m, d] float32 and shared by every (b, h).
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *    work is enqueued on it asynchronously; no entry point synchronises.
+ *  - Every argument check runs on the host before anything is enqueued and
+ *    returns a negative favor_status; nothing is launched in that case.  A
+ *    launch failure reported by the HIP runtime returns FAVOR_ERR_HIP.  No
+ *    C++ exception crosses this interface.
+ *  - Non-finite inputs propagate as IEEE values; a query whose estimated
+ *    denominator phi(q)^T z is zero yields 0/0 = NaN (the method has no
+ *    epsilon in the normaliser).
+ */
+#ifndef FAVOR_H_
+#define FAVOR_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FAVOR_OK = 0,
+  FAVOR_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum   */
+  FAVOR_ERR_UNSUPPORTED = -2,   /* valid request this build cannot run     */
+  FAVOR_ERR_WORKSPACE = -3,     /* workspace missing or smaller than asked */
+  FAVOR_ERR_ALIAS = -4,         /* an output overlaps an input/workspace   */
+  FAVOR_ERR_HIP = -5            /* the HIP runtime reported an error       */
+} favor_status;
+
+typedef enum { FAVOR_DTYPE_F32 = 0, FAVOR_DTYPE_BF16 = 1 } favor_dtype;
+
+/* Feature maps.
+ * TRIG: phi(x) = exp(|x~|^2/2) m^-1/2 [sin(Omega x~), cos(Omega x~)],
+ *       F = 2m features, an unbiased estimate of exp(q.k/sqrt(d))
+ *       (FAVOR+ blog page, section 核心机制：FAVOR+, trigonometric mode).
+ * RELU: phi(x) = m^-1/2 max(Omega x~, 0), F = m features: generalized
+ *       attention with ReLU as the kernel function (Chinese summary page,
+ *       section 核心创新 item 2; English page, Technical Contribution).
+ * In both, x~ = d^-1/4 x is applied by the library to the Q and K passed in. */
+typedef enum { FAVOR_FEATURE_TRIG = 0, FAVOR_FEATURE_RELU = 1 } favor_feature_kind;
+
+/* Kernel family selection for favor_attention_ex (AUTO = the fastest path
+ * that supports the request).  MFMA requires bf16, d = 64 and m a multiple
+ * of 32 with m <= 512; GENERIC handles f32 and bf16 with d <= 64. */
+typedef enum { FAVOR_PATH_AUTO = 0, FAVOR_PATH_GENERIC = 1, FAVOR_PATH_MFMA = 2 } favor_path;
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int favor_version(void);
+
+/* Static, human-readable text for a favor_status value. */
+const char* favor_status_string(int status);
+
+/*
+ * favor_orf_omega -- orthogonal random features (HOST function).
+ * Builds Omega [m, d] (float32, host memory, written by the call) from raw
+ * Gaussian draws: for each d x d block of `gaussian` ([n_blocks, d, d]
+ * float64, host, n_blocks = ceil(m / d)) the rows are orthonormalised in
+ * order by modified Gram-Schmidt in float64; row r of the stacked result is
+ * scaled to the chi(d) radius radii[r] ([m] float64, host) and rounded to
+ * float32; the first m rows are kept.  Rows within a block are mutually
+ * orthogonal and each row is marginally N(0, I_d) (FAVOR+ blog page,
+ * section 核心机制：FAVOR+, orthogonal random directions; Chinese summary
+ * page, section 方法详解).
+ * Errors: FAVOR_ERR_INVALID_ARG for null pointers or m, d < 1, or a block
+ * whose rows are linearly dependent.  Touches no device.
+ */
+int favor_orf_omega(const double* gaussian, const double* radii, int m, int d, float* omega);
+
+/*
+ * Workspace (device memory, bytes) that favor_attention needs for this
+ * request; 0 is possible.  Returns 0 also for an invalid request (the call
+ * itself then reports the error).  `path` as in favor_attention_ex.
+ */
+size_t favor_attention_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
+                                       int kind, int causal);
+size_t favor_attention_workspace_bytes_ex(int B, int H, int L, int d, int m, int dtype,
+                                          int kind, int causal, int path);
+
+/*
+ * favor_attention -- FAVOR attention, out = D^-1 (phi(Q) phi(K)^T) V
+ * evaluated in linear order (FAVOR+ blog page, section 核心机制：FAVOR+).
+ *   Q, K, V : [B, H, L, d] device, element type `dtype` (float32 or bf16)
+ *   Omega   : [m, d] float32 device, shared by every (b, h)
+ *   out     : [B, H, L, d] device, element type `dtype`; fully written.
+ *             Must not overlap Q, K, V, Omega or the workspace.
+ *   kind    : favor_feature_kind; causal: 0 = bidirectional,
+ *             1 = causal (inclusive prefix over j <= i).
+ *   workspace / workspace_bytes : device scratch of at least
+ *             favor_attention_workspace_bytes(...) bytes (NULL if 0);
+ *             contents on entry are ignored; clobbered.
+ * B, H, L >= 0 (any zero makes the call a no-op returning FAVOR_OK);
+ * d in [1, 64]; m >= 1 (m <= 1024).  Accumulation is float32 in every path.
+ * Returns FAVOR_OK or a negative favor_status (see the conventions above).
+ */
+int favor_attention(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                    int B, int H, int L, int d, int m, int dtype, int kind, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* As favor_attention, with an explicit kernel family (favor_path).  A path
+ * that cannot run the request returns FAVOR_ERR_UNSUPPORTED. */
+int favor_attention_ex(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                       int B, int H, int L, int d, int m, int dtype, int kind, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream, int path);
+
+/* The favor_path that favor_attention_ex(..., path) would run (GENERIC or
+ * MFMA), or a negative favor_status if the request is invalid/unsupported. */
+int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, int kind,
+                                 int causal, int path);
+
+/*
+ * favor_profile_attention -- per-kernel timing of favor_attention_ex.
+ * Enqueues `iters` back-to-back calls on `stream`, recording a HIP event
+ * before and after every kernel, waits for them, and writes the mean
+ * duration in milliseconds of each kernel (phase) of one call to
+ * phase_ms[0 .. *n_phases-1] and a short name of each into names
+ * (max_phases entries of 48 bytes, NUL-terminated).  Creates and destroys
+ * its own events; synchronises the stream.  Arguments as favor_attention_ex.
+ */
+int favor_profile_attention(const void* Q, const void* K, const void* V, const float* Omega,
+                            void* out, int B, int H, int L, int d, int m, int dtype, int kind,
+                            int causal, void* workspace, size_t workspace_bytes, void* stream,
+                            int path, int iters, float* phase_ms, char* names, int max_phases,
+                            int* n_phases);
+
+/*
+ * Masked-LM attention block helpers (bf16), for the Performer block whose
+ * attention is FAVOR ("Masked Language Modeling for Proteins ..." summary
+ * pages, Methodology / 实验设计: protein sequences, multi-head attention).
+ *
+ * favor_embed_bf16: x[t, :] = table[ids[t], :] for t < n_tok.
+ *   ids int32 [n_tok] device; table bf16 [vocab, E] device; x bf16
+ *   [n_tok, E] device.  An id outside [0, vocab) writes a zero row.
+ */
+int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int vocab, int E,
+                     void* stream);
+
+/*
+ * favor_linear_bf16: Y = X W (bf16 operands, float32 accumulation on MFMA,
+ * one round-to-nearest-even to bf16 at the end).  W is [K, N] row-major.
+ *   X: logical [M, K].  in_heads == 0: X is [M, K] row-major.  in_heads > 0:
+ *      X is head-split [M / seq_len, in_heads, seq_len, K / in_heads] and
+ *      logical row r = b * seq_len + t gathers the heads' rows in order.
+ *   Y: logical [M, N], stored row-major when out_heads == 0, or head-split
+ *      [M / seq_len, out_heads, seq_len, N / out_heads] when out_heads > 0.
+ * Requires M, N, K >= 1, N and K multiples of 32 (of 32 * heads when
+ * split) and M a multiple of seq_len when a split is used; Y must not
+ * overlap X or W.
+ */
+int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K, int in_heads,
+                      int out_heads, int seq_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FAVOR_H_ */

@@ -1,0 +1,265 @@
+"""ctypes binding of libfavor.so (include/favor.h).
+
+Argument marshalling only: every arithmetic step runs in the library's
+HIP kernels.  torch is used for device memory (tensors, workspace) and
+for the current HIP stream.  There is no CPU fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfavor.so")
+
+FAVOR_OK = 0
+FAVOR_ERR_INVALID_ARG = -1
+FAVOR_ERR_UNSUPPORTED = -2
+FAVOR_ERR_WORKSPACE = -3
+FAVOR_ERR_ALIAS = -4
+FAVOR_ERR_HIP = -5
+
+DTYPE = {"f32": 0, "bf16": 1}
+KIND = {"trig": 0, "relu": 1}
+PATH = {"auto": 0, "generic": 1, "mfma": 2}
+PATH_NAME = {v: k for k, v in PATH.items()}
+
+EXPORTS = (
+    "favor_version", "favor_status_string", "favor_orf_omega",
+    "favor_attention_workspace_bytes", "favor_attention_workspace_bytes_ex",
+    "favor_attention", "favor_attention_ex", "favor_attention_resolve_path",
+    "favor_profile_attention", "favor_embed_bf16", "favor_linear_bf16",
+)
+
+
+class FavorError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    i, z, p = _c_int, _c_size, _vp
+    sig = {
+        "favor_version": (i, []),
+        "favor_status_string": (ctypes.c_char_p, [i]),
+        "favor_orf_omega": (i, [p, p, i, i, p]),
+        "favor_attention_workspace_bytes": (z, [i] * 8),
+        "favor_attention_workspace_bytes_ex": (z, [i] * 9),
+        "favor_attention": (i, [p, p, p, p, p] + [i] * 8 + [p, z, p]),
+        "favor_attention_ex": (i, [p, p, p, p, p] + [i] * 8 + [p, z, p, i]),
+        "favor_attention_resolve_path": (i, [i] * 9),
+        "favor_profile_attention": (i, [p, p, p, p, p] + [i] * 8 + [p, z, p, i, i, p, p, i, p]),
+        "favor_embed_bf16": (i, [p, p, p, i, i, i, p]),
+        "favor_linear_bf16": (i, [p, p, p, i, i, i, i, i, i, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfavor.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m linear_kernelized_attention_amd.build`")
+        import torch  # noqa: F401  -- load torch's HIP runtime first
+        handle = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+        _declare(handle)
+        _lib = handle
+    return _lib
+
+
+def loaded_hip_runtimes() -> List[str]:
+    """Paths of every libamdhip64 mapped in this process (should be one)."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(line.split()[-1])
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+def status_string(status: int) -> str:
+    return lib().favor_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != FAVOR_OK:
+        raise FavorError(status, what)
+
+
+# ----------------------------------------------------------------- host ORF
+def favor_orf_omega(gaussian: np.ndarray, radii: np.ndarray, m: int) -> np.ndarray:
+    """Omega [m, d] float32 from raw Gaussian blocks and chi(d) radii."""
+    g = np.ascontiguousarray(gaussian, dtype=np.float64)
+    r = np.ascontiguousarray(radii, dtype=np.float64)
+    n_blocks, d, d2 = g.shape
+    if d != d2 or n_blocks * d < m or r.size < m:
+        raise ValueError("gaussian must be [ceil(m/d), d, d] and radii [m]")
+    out = np.empty((m, d), dtype=np.float32)
+    _check(lib().favor_orf_omega(g.ctypes.data, r.ctypes.data, int(m), int(d), out.ctypes.data),
+           "favor_orf_omega")
+    return out
+
+
+# ----------------------------------------------------------------- attention
+def _torch_dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return DTYPE["f32"]
+    if t.dtype == torch.bfloat16:
+        return DTYPE["bf16"]
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream_ptr(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _validate(q, k, v, omega):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("omega", omega)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, L, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if omega.dtype != torch.float32 or omega.dim() != 2 or omega.shape[1] != q.shape[3]:
+        raise ValueError("omega must be float32 [m, d]")
+    if not (q.device == k.device == v.device == omega.device):
+        raise ValueError("all tensors must be on one device")
+
+
+def favor_attention_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="trig", causal=False,
+                                    path="auto") -> int:
+    return int(lib().favor_attention_workspace_bytes_ex(
+        B, H, L, d, m, DTYPE[dtype], KIND[kind], int(bool(causal)), PATH[path]))
+
+
+def favor_attention_resolve_path(B, H, L, d, m, dtype="bf16", kind="trig", causal=False,
+                                 path="auto") -> str:
+    r = lib().favor_attention_resolve_path(B, H, L, d, m, DTYPE[dtype], KIND[kind],
+                                           int(bool(causal)), PATH[path])
+    _check(FAVOR_OK if r > 0 else r, "favor_attention_resolve_path")
+    return PATH_NAME[r]
+
+
+def _call_args(q, k, v, omega, kind, causal, path, out, workspace):
+    import torch
+    _validate(q, k, v, omega)
+    B, H, L, d = q.shape
+    m = omega.shape[0]
+    dt = _torch_dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    need = int(lib().favor_attention_workspace_bytes_ex(B, H, L, d, m, dt, KIND[kind],
+                                                        int(bool(causal)), PATH[path]))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(), out.data_ptr(),
+            B, H, L, d, m, dt, KIND[kind], int(bool(causal)),
+            workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device), PATH[path]]
+    return args, out, workspace
+
+
+def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, path: str = "auto",
+                    out=None, workspace=None):
+    """FAVOR attention of [B, H, L, d] float32/bf16 tensors on the GPU."""
+    args, out, _ = _call_args(q, k, v, omega, kind, causal, path, out, workspace)
+    _check(lib().favor_attention_ex(*args), "favor_attention")
+    return out
+
+
+def favor_profile_attention(q, k, v, omega, kind="trig", causal=False, path="auto", iters=20,
+                            out=None, workspace=None) -> List[Tuple[str, float]]:
+    """[(kernel name, mean ms per call)] measured with HIP events."""
+    args, out, _ = _call_args(q, k, v, omega, kind, causal, path, out, workspace)
+    max_ph = 8
+    ms = (ctypes.c_float * max_ph)()
+    names = ctypes.create_string_buffer(48 * max_ph)
+    n = ctypes.c_int(0)
+    _check(lib().favor_profile_attention(*args, int(iters), ms, names, max_ph, ctypes.byref(n)),
+           "favor_profile_attention")
+    res = []
+    for i in range(n.value):
+        nm = names.raw[48 * i:48 * (i + 1)].split(b"\0", 1)[0].decode()
+        res.append((nm, float(ms[i])))
+    return res
+
+
+# ------------------------------------------------------------ block helpers
+def favor_embed_bf16(ids, table, out=None):
+    import torch
+    if ids.dtype != torch.int32 or table.dtype != torch.bfloat16:
+        raise TypeError("ids must be int32 and table bfloat16")
+    if not ids.is_contiguous() or not table.is_contiguous():
+        raise ValueError("ids and table must be contiguous")
+    n_tok = ids.numel()
+    vocab, E = table.shape
+    if out is None:
+        out = torch.empty(*ids.shape, E, dtype=torch.bfloat16, device=table.device)
+    _check(lib().favor_embed_bf16(ids.data_ptr(), table.data_ptr(), out.data_ptr(), n_tok, vocab, E,
+                                  _stream_ptr(table.device)), "favor_embed_bf16")
+    return out
+
+
+def favor_linear_bf16(x, w, M: int, N: int, K: int, in_heads: int = 0, out_heads: int = 0,
+                      seq_len: int = 0, out=None):
+    """Y = X W with optional head-split layouts (see include/favor.h)."""
+    import torch
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x and w must be contiguous")
+    if x.numel() != M * K or w.numel() != K * N:
+        raise ValueError("x must hold M*K and w K*N elements")
+    if out is None:
+        out = torch.empty(M * N, dtype=torch.bfloat16, device=x.device)
+    elif out.numel() != M * N:
+        raise ValueError("out must hold M*N elements")
+    _check(lib().favor_linear_bf16(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, in_heads,
+                                   out_heads, seq_len, _stream_ptr(x.device)), "favor_linear_bf16")
+    return out
+
+
+def favor_performer_block(ids, embed, wq, wk, wv, wo, omega, heads: int, kind: str = "relu",
+                          path: str = "auto"):
+    """Masked-LM attention block: gather, Q/K/V projections written head-split,
+    FAVOR attention, output projection reading the head-split result."""
+    import torch
+    B, L = ids.shape
+    E = embed.shape[1]
+    dh = E // heads
+    M = B * L
+    x = favor_embed_bf16(ids, embed)
+    proj = []
+    for w in (wq, wk, wv):
+        y = favor_linear_bf16(x, w, M, E, E, 0, heads, L)
+        proj.append(y.view(B, heads, L, dh))
+    o = favor_attention(proj[0], proj[1], proj[2], omega, kind=kind, causal=False, path=path)
+    y = favor_linear_bf16(o, wo, M, E, E, heads, 0, L)
+    return y.view(B, L, E)

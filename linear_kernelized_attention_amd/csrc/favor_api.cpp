@@ -1,0 +1,287 @@
+// Host side of the C ABI declared in include/favor.h: argument checks,
+// kernel-family selection, workspace sizing and per-kernel profiling.
+// Nothing here allocates device memory.
+#include "favor.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+#include "favor_internal.h"
+
+using favor::Problem;
+
+namespace {
+
+constexpr int kVersion = (0 << 16) | (3 << 8) | 0;
+constexpr int kMaxD = 64;
+constexpr int kMaxM = 1024;
+
+bool valid_enums(int dtype, int kind, int causal) {
+  return (dtype == FAVOR_DTYPE_F32 || dtype == FAVOR_DTYPE_BF16) &&
+         (kind == FAVOR_FEATURE_TRIG || kind == FAVOR_FEATURE_RELU) && (causal == 0 || causal == 1);
+}
+
+// Shape/enum checks shared by sizing and launching.  Returns FAVOR_OK,
+// or a negative status; *empty is set when B*H*L == 0.
+int check_problem(int B, int H, int L, int d, int m, int dtype, int kind, int causal, Problem* p,
+                  bool* empty) {
+  if (B < 0 || H < 0 || L < 0 || d < 1 || m < 1) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_enums(dtype, kind, causal)) return FAVOR_ERR_INVALID_ARG;
+  const long long elems = (long long)B * H * (long long)L * d;
+  if (elems > (1LL << 40)) return FAVOR_ERR_UNSUPPORTED;
+  if (d > kMaxD || m > kMaxM) return FAVOR_ERR_UNSUPPORTED;
+  p->B = B; p->H = H; p->L = L; p->d = d; p->m = m;
+  p->dtype = dtype; p->kind = kind; p->causal = causal;
+  p->BH = (long long)B * H;
+  p->F = kind == FAVOR_FEATURE_TRIG ? 2 * m : m;
+  *empty = (elems == 0);
+  if (!*empty && p->BH > 65535LL * 64) return FAVOR_ERR_UNSUPPORTED;
+  return FAVOR_OK;
+}
+
+int resolve(const Problem& p, int path) {
+  switch (path) {
+    case FAVOR_PATH_AUTO:
+      if (favor::mfma::supports(p)) return FAVOR_PATH_MFMA;
+      if (favor::generic::supports(p)) return FAVOR_PATH_GENERIC;
+      return FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_GENERIC:
+      return favor::generic::supports(p) ? FAVOR_PATH_GENERIC : FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_MFMA:
+      return favor::mfma::supports(p) ? FAVOR_PATH_MFMA : FAVOR_ERR_UNSUPPORTED;
+    default:
+      return FAVOR_ERR_INVALID_ARG;
+  }
+}
+
+size_t ws_bytes(const Problem& p, int resolved) {
+  return resolved == FAVOR_PATH_MFMA ? favor::mfma::workspace_bytes(p)
+                                     : favor::generic::workspace_bytes(p);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct Checked {
+  Problem p;
+  int path;
+  bool empty;
+};
+
+int check_call(const void* Q, const void* K, const void* V, const float* Omega, void* out, int B,
+               int H, int L, int d, int m, int dtype, int kind, int causal, void* ws,
+               size_t ws_bytes_given, int path, Checked* c) {
+  int st = check_problem(B, H, L, d, m, dtype, kind, causal, &c->p, &c->empty);
+  if (st != FAVOR_OK) return st;
+  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (c->empty) {
+    c->path = FAVOR_PATH_GENERIC;
+    return FAVOR_OK;
+  }
+  if (!Q || !K || !V || !Omega || !out) return FAVOR_ERR_INVALID_ARG;
+  const int r = resolve(c->p, path);
+  if (r < 0) return r;
+  c->path = r;
+  const size_t need = ws_bytes(c->p, r);
+  if (need > 0 && (!ws || ws_bytes_given < need)) return FAVOR_ERR_WORKSPACE;
+  const size_t esz = dtype == FAVOR_DTYPE_F32 ? 4 : 2;
+  const size_t tensor = (size_t)c->p.BH * (size_t)L * (size_t)d * esz;
+  const size_t omega_b = (size_t)m * d * sizeof(float);
+  if (overlaps(out, tensor, Q, tensor) || overlaps(out, tensor, K, tensor) ||
+      overlaps(out, tensor, V, tensor) || overlaps(out, tensor, Omega, omega_b))
+    return FAVOR_ERR_ALIAS;
+  if (need > 0 && (overlaps(ws, need, Q, tensor) || overlaps(ws, need, K, tensor) ||
+                   overlaps(ws, need, V, tensor) || overlaps(ws, need, Omega, omega_b) ||
+                   overlaps(ws, need, out, tensor)))
+    return FAVOR_ERR_ALIAS;
+  return FAVOR_OK;
+}
+
+int launch(const Checked& c, const void* Q, const void* K, const void* V, const float* Omega,
+           void* out, void* ws, size_t wsb, hipStream_t s, favor::PhaseHook* hook) {
+  favor::Buffers b{Q, K, V, Omega, out, ws, wsb};
+  hipError_t e = c.path == FAVOR_PATH_MFMA ? favor::mfma::run(c.p, b, s, hook)
+                                           : favor::generic::run(c.p, b, s, hook);
+  if (e != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipPeekAtLastError() != hipSuccess) {
+    (void)hipGetLastError();
+    return FAVOR_ERR_HIP;
+  }
+  return FAVOR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int favor_version(void) { return kVersion; }
+
+const char* favor_status_string(int status) {
+  switch (status) {
+    case FAVOR_OK: return "ok";
+    case FAVOR_ERR_INVALID_ARG: return "invalid argument";
+    case FAVOR_ERR_UNSUPPORTED: return "unsupported shape, dtype or path";
+    case FAVOR_ERR_WORKSPACE: return "workspace missing or too small";
+    case FAVOR_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case FAVOR_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int favor_orf_omega(const double* gaussian, const double* radii, int m, int d, float* omega) {
+  if (!gaussian || !radii || !omega || m < 1 || d < 1) return FAVOR_ERR_INVALID_ARG;
+  const int n_blocks = (m + d - 1) / d;
+  std::vector<double> blk((size_t)d * d);
+  for (int b = 0; b < n_blocks; ++b) {
+    std::memcpy(blk.data(), gaussian + (size_t)b * d * d, sizeof(double) * d * d);
+    // Modified Gram-Schmidt over the rows, in order.
+    for (int r = 0; r < d; ++r) {
+      double* row = blk.data() + (size_t)r * d;
+      for (int s = 0; s < r; ++s) {
+        const double* prev = blk.data() + (size_t)s * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += row[c] * prev[c];
+        for (int c = 0; c < d; ++c) row[c] -= dot * prev[c];
+      }
+      double nrm = 0.0;
+      for (int c = 0; c < d; ++c) nrm += row[c] * row[c];
+      nrm = std::sqrt(nrm);
+      if (!(nrm > 0.0) || !std::isfinite(nrm)) return FAVOR_ERR_INVALID_ARG;
+      for (int c = 0; c < d; ++c) row[c] /= nrm;
+      const int out_row = b * d + r;
+      if (out_row >= m) continue;
+      for (int c = 0; c < d; ++c) omega[(size_t)out_row * d + c] = (float)(row[c] * radii[out_row]);
+    }
+  }
+  return FAVOR_OK;
+}
+
+size_t favor_attention_workspace_bytes_ex(int B, int H, int L, int d, int m, int dtype, int kind,
+                                          int causal, int path) {
+  Problem p;
+  bool empty;
+  if (check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty) != FAVOR_OK || empty) return 0;
+  const int r = resolve(p, path);
+  return r < 0 ? 0 : ws_bytes(p, r);
+}
+
+size_t favor_attention_workspace_bytes(int B, int H, int L, int d, int m, int dtype, int kind,
+                                       int causal) {
+  return favor_attention_workspace_bytes_ex(B, H, L, d, m, dtype, kind, causal, FAVOR_PATH_AUTO);
+}
+
+int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, int kind,
+                                 int causal, int path) {
+  Problem p;
+  bool empty;
+  int st = check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty);
+  if (st != FAVOR_OK) return st;
+  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  return resolve(p, path);
+}
+
+int favor_attention_ex(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                       int B, int H, int L, int d, int m, int dtype, int kind, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream, int path) {
+  Checked c;
+  int st = check_call(Q, K, V, Omega, out, B, H, L, d, m, dtype, kind, causal, workspace,
+                      workspace_bytes, path, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  return launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+}
+
+int favor_attention(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                    int B, int H, int L, int d, int m, int dtype, int kind, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return favor_attention_ex(Q, K, V, Omega, out, B, H, L, d, m, dtype, kind, causal, workspace,
+                            workspace_bytes, stream, FAVOR_PATH_AUTO);
+}
+
+int favor_profile_attention(const void* Q, const void* K, const void* V, const float* Omega,
+                            void* out, int B, int H, int L, int d, int m, int dtype, int kind,
+                            int causal, void* workspace, size_t workspace_bytes, void* stream,
+                            int path, int iters, float* phase_ms, char* names, int max_phases,
+                            int* n_phases) {
+  if (iters < 1 || !phase_ms || max_phases < 1 || !n_phases) return FAVOR_ERR_INVALID_ARG;
+  Checked c;
+  int st = check_call(Q, K, V, Omega, out, B, H, L, d, m, dtype, kind, causal, workspace,
+                      workspace_bytes, path, &c);
+  if (st != FAVOR_OK) return st;
+  *n_phases = 0;
+  if (c.empty) return FAVOR_OK;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<hipEvent_t> ev((size_t)iters * 2 * max_phases, nullptr);
+  int rc = FAVOR_OK;
+  for (auto& e : ev) {
+    if (hipEventCreate(&e) != hipSuccess) { e = nullptr; rc = FAVOR_ERR_HIP; break; }
+  }
+  int phases = 0;
+  std::vector<double> sum(max_phases, 0.0);
+  if (rc == FAVOR_OK) {
+    for (int it = 0; it < iters && rc == FAVOR_OK; ++it) {
+      favor::PhaseHook hook{ev.data() + (size_t)it * 2 * max_phases, max_phases, 0,
+                            it == 0 ? names : nullptr};
+      rc = launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, s, &hook);
+      phases = hook.n;
+    }
+    if (rc == FAVOR_OK && hipStreamSynchronize(s) != hipSuccess) rc = FAVOR_ERR_HIP;
+    if (rc == FAVOR_OK) {
+      for (int it = 0; it < iters && rc == FAVOR_OK; ++it)
+        for (int ph = 0; ph < phases; ++ph) {
+          float ms = 0.f;
+          const size_t base = (size_t)it * 2 * max_phases;
+          if (hipEventElapsedTime(&ms, ev[base + 2 * ph], ev[base + 2 * ph + 1]) != hipSuccess) {
+            rc = FAVOR_ERR_HIP;
+            break;
+          }
+          sum[ph] += ms;
+        }
+    }
+  }
+  for (auto& e : ev)
+    if (e) hipEventDestroy(e);
+  if (rc != FAVOR_OK) return rc;
+  for (int ph = 0; ph < phases; ++ph) phase_ms[ph] = (float)(sum[ph] / iters);
+  *n_phases = phases;
+  return FAVOR_OK;
+}
+
+int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int vocab, int E,
+                     void* stream) {
+  if (n_tok < 0 || vocab < 1 || E < 1) return FAVOR_ERR_INVALID_ARG;
+  if (n_tok == 0) return FAVOR_OK;
+  if (!ids || !table || !x) return FAVOR_ERR_INVALID_ARG;
+  if (overlaps(x, (size_t)n_tok * E * 2, table, (size_t)vocab * E * 2) ||
+      overlaps(x, (size_t)n_tok * E * 2, ids, (size_t)n_tok * 4))
+    return FAVOR_ERR_ALIAS;
+  hipError_t e = favor::block::embed(ids, (const uint16_t*)table, (uint16_t*)x, n_tok, vocab, E,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K, int in_heads,
+                      int out_heads, int seq_len, void* stream) {
+  if (M < 1 || N < 1 || K < 1 || in_heads < 0 || out_heads < 0) return FAVOR_ERR_INVALID_ARG;
+  if (!X || !W || !Y) return FAVOR_ERR_INVALID_ARG;
+  if (N % 32 || K % 32) return FAVOR_ERR_UNSUPPORTED;
+  if (in_heads > 0 || out_heads > 0) {
+    if (seq_len < 1 || M % seq_len) return FAVOR_ERR_INVALID_ARG;
+    if (in_heads > 0 && K % (32 * in_heads)) return FAVOR_ERR_UNSUPPORTED;
+    if (out_heads > 0 && N % (32 * out_heads)) return FAVOR_ERR_UNSUPPORTED;
+  }
+  if ((long long)M * N > (1LL << 40) || (long long)M * K > (1LL << 40)) return FAVOR_ERR_UNSUPPORTED;
+  if (overlaps(Y, (size_t)M * N * 2, X, (size_t)M * K * 2) ||
+      overlaps(Y, (size_t)M * N * 2, W, (size_t)K * N * 2))
+    return FAVOR_ERR_ALIAS;
+  hipError_t e = favor::block::linear((const uint16_t*)X, (const uint16_t*)W, (uint16_t*)Y, M, N, K,
+                                      in_heads, out_heads, seq_len, (hipStream_t)stream);
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+}  // extern "C"

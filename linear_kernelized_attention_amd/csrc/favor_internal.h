@@ -1,0 +1,77 @@
+// Internal interface between the C-ABI host dispatch and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace favor {
+
+enum { KIND_TRIG = 0, KIND_RELU = 1 };
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { PATH_AUTO = 0, PATH_GENERIC = 1, PATH_MFMA = 2 };
+
+struct Problem {
+  int B, H, L, d, m, dtype, kind, causal;
+  long long BH;  // B * H
+  int F;         // feature width: 2m (trig) or m (relu)
+};
+
+struct Buffers {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* omega;
+  void* out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Optional per-kernel event recording (used by favor_profile_attention).
+struct PhaseHook {
+  hipEvent_t* ev;  // 2 * max_phases events: begin/end of each phase
+  int max_phases;
+  int n;
+  char* names;     // max_phases * 48 bytes, may be null
+};
+
+inline void phase_begin(PhaseHook* h, hipStream_t s, const char* name) {
+  if (!h || h->n >= h->max_phases) return;
+  hipEventRecord(h->ev[2 * h->n], s);
+  if (h->names) {
+    char* dst = h->names + 48 * h->n;
+    int i = 0;
+    for (; name[i] && i < 47; ++i) dst[i] = name[i];
+    dst[i] = 0;
+  }
+}
+
+inline void phase_end(PhaseHook* h, hipStream_t s) {
+  if (!h || h->n >= h->max_phases) return;
+  hipEventRecord(h->ev[2 * h->n + 1], s);
+  ++h->n;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+namespace generic {
+bool supports(const Problem& p);
+size_t workspace_bytes(const Problem& p);
+hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+}  // namespace generic
+
+namespace mfma {
+bool supports(const Problem& p);
+size_t workspace_bytes(const Problem& p);
+hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+}  // namespace mfma
+
+namespace block {
+hipError_t embed(const int* ids, const uint16_t* table, uint16_t* x, int n_tok, int vocab, int E,
+                 hipStream_t s);
+hipError_t linear(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K,
+                  int in_heads, int out_heads, int seq_len, hipStream_t s);
+}  // namespace block
+
+}  // namespace favor

@@ -1,0 +1,39 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device and
+compare with the oracle using the per-(b, h) relative Frobenius error."""
+import numpy as np
+import torch
+
+import linear_kernelized_attention_amd as F
+from linear_kernelized_attention_amd import inputs as I
+from oracle import favor_oracle as O
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    bits = np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(bits).cuda().view(torch.bfloat16)
+
+
+def from_device(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def problem(B, H, L, d, m, dtype, seed=0, norm_shells=False):
+    """(device q, k, v, omega; float64 q, k, v; oracle Omega)."""
+    a = I.attention_inputs(B, H, L, d, dtype, seed=seed, norm_shells=norm_shells)
+    dr = I.omega_draws(m, d, seed=seed)
+    omega_dev = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, m)).cuda()
+    omega_ref = O.orthogonal_random_features(dr.gaussian, dr.radii, m)
+    dev = tuple(to_device(x, dtype) for x in (a.q, a.k, a.v)) + (omega_dev,)
+    return dev, (a.q64, a.k64, a.v64), omega_ref
+
+
+def slice_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over leading (b, h) slices of |got - ref|_F / |ref|_F."""
+    g = got.reshape(-1, *got.shape[-2:])
+    r = ref.reshape(-1, *ref.shape[-2:])
+    errs = [np.linalg.norm(g[i] - r[i]) / np.linalg.norm(r[i]) for i in range(g.shape[0])]
+    return float(max(errs))

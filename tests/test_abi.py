@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/favor.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_kernelized_attention_amd as F
+from linear_kernelized_attention_amd import _lib as B
+from linear_kernelized_attention_amd import inputs as I
+from oracle import favor_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "favor.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(favor_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_exported():
+    lib = F.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_single_hip_runtime():
+    F.lib()
+    assert len(F.loaded_hip_runtimes()) <= 1
+
+
+def test_version_and_status_strings():
+    lib = F.lib()
+    assert lib.favor_version() > 0
+    for s in (0, -1, -2, -3, -4, -5):
+        assert F.status_string(s) and F.status_string(s) != "unknown status"
+    assert F.status_string(7) == "unknown status"
+
+
+# Fake, never-dereferenced addresses: every call below must return before
+# touching memory or launching anything.
+QA, KA, VA, WA, OA, WS = (0x100000 * i for i in range(1, 7))
+
+
+def call(q=QA, k=KA, v=VA, w=WA, o=OA, B_=2, H=2, L=64, d=64, m=256, dt=1, kind=0, causal=0,
+         ws=WS, wsb=1 << 30, path=0):
+    return F.lib().favor_attention_ex(q, k, v, w, o, B_, H, L, d, m, dt, kind, causal, ws, wsb, None,
+                                      path)
+
+
+def test_invalid_arguments():
+    assert call(q=0) == B.FAVOR_ERR_INVALID_ARG
+    assert call(o=0) == B.FAVOR_ERR_INVALID_ARG
+    assert call(w=0) == B.FAVOR_ERR_INVALID_ARG
+    assert call(B_=-1) == B.FAVOR_ERR_INVALID_ARG
+    assert call(d=0) == B.FAVOR_ERR_INVALID_ARG
+    assert call(m=0) == B.FAVOR_ERR_INVALID_ARG
+    assert call(dt=2) == B.FAVOR_ERR_INVALID_ARG
+    assert call(kind=5) == B.FAVOR_ERR_INVALID_ARG
+    assert call(causal=2) == B.FAVOR_ERR_INVALID_ARG
+    assert call(path=9) == B.FAVOR_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_noop():
+    for kw in (dict(L=0), dict(B_=0), dict(H=0)):
+        assert call(q=0, k=0, v=0, w=0, o=0, ws=0, wsb=0, **kw) == B.FAVOR_OK
+
+
+def test_unsupported():
+    assert call(d=128) == B.FAVOR_ERR_UNSUPPORTED
+    assert call(m=4096) == B.FAVOR_ERR_UNSUPPORTED
+    # the MFMA family needs bf16 and d = 64
+    assert call(dt=0, d=16, m=64, path=2) == B.FAVOR_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    need = F.favor_attention_workspace_bytes(2, 2, 64, 64, 256, "bf16", "trig", False)
+    assert need > 0
+    assert call(ws=0) == B.FAVOR_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.FAVOR_ERR_WORKSPACE
+
+
+def test_alias_checks():
+    assert call(o=QA) == B.FAVOR_ERR_ALIAS
+    assert call(o=VA + 64) == B.FAVOR_ERR_ALIAS
+    assert call(ws=OA) == B.FAVOR_ERR_ALIAS
+
+
+def test_workspace_sizes_monotone():
+    a = F.favor_attention_workspace_bytes(1, 8, 4096, 64, 256, "bf16", "trig", True)
+    b = F.favor_attention_workspace_bytes(1, 8, 32768, 64, 256, "bf16", "trig", True)
+    assert 0 < a <= b
+    assert F.favor_attention_workspace_bytes(1, 1, 512, 16, 64, "f32", "trig", False) > 0
+    assert F.favor_attention_workspace_bytes(1, 1, 0, 16, 64, "f32", "trig", False) == 0
+
+
+def test_resolve_path():
+    assert F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False) == "generic"
+    assert F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False, "generic") == "generic"
+    with pytest.raises(F.FavorError):
+        F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False, "mfma")
+
+
+def test_linear_and_embed_argument_checks():
+    lib = F.lib()
+    assert lib.favor_linear_bf16(QA, KA, OA, 0, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_linear_bf16(QA, KA, OA, 64, 48, 64, 0, 0, 0, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_linear_bf16(QA, KA, QA, 64, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_ALIAS
+    assert lib.favor_linear_bf16(QA, KA, OA, 100, 64, 64, 0, 2, 64, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_embed_bf16(0, KA, OA, 10, 26, 512, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_embed_bf16(0, 0, 0, 0, 26, 512, None) == B.FAVOR_OK
+
+
+@pytest.mark.parametrize("m,d", [(64, 16), (256, 64), (40, 16)])
+def test_host_orf_matches_oracle(m, d):
+    # the library's host ORF (float64 Gram-Schmidt, float32 output) against
+    # the oracle's, from the same raw draws
+    dr = I.omega_draws(m, d, seed=0)
+    ours = F.favor_orf_omega(dr.gaussian, dr.radii, m)
+    ref = O.orthogonal_random_features(dr.gaussian, dr.radii, m)
+    assert ours.dtype == np.float32 and ours.shape == (m, d)
+    assert np.abs(ours - ref).max() <= 4e-7 * np.abs(ref).max()
+
+
+def test_host_orf_rejects_degenerate_block():
+    g = np.zeros((1, 4, 4))
+    with pytest.raises(F.FavorError):
+        F.favor_orf_omega(g, np.ones(4), 4)

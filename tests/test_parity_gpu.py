@@ -1,0 +1,149 @@
+"""GPU vs oracle parity for favor_attention, through the C ABI.
+
+Bar: per-(b, h) relative Frobenius error <= 1e-4 for float32 inputs and
+<= 2e-2 for bf16 inputs.  Small and ragged shapes are compared on every
+element; the full-size long-sequence workloads on sampled rows that the
+oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import linear_kernelized_attention_amd as F
+from linear_kernelized_attention_amd import inputs as I
+from oracle import favor_oracle as O
+from tests.gpu_util import TOL, from_device, problem, slice_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _paths(B, H, L, d, m, dtype, kind, causal):
+    paths = ["generic"]
+    if F.favor_attention_resolve_path(B, H, L, d, m, dtype, kind, causal) == "mfma":
+        paths.append("mfma")
+    return paths
+
+
+def _run(dev, kind, causal, path):
+    out = F.favor_attention(*dev, kind=kind, causal=causal, path=path)
+    torch.cuda.synchronize()
+    return from_device(out)
+
+
+SMALL = [
+    # B, H, L, d, m, dtype
+    (1, 1, 1, 16, 64, "f32"),
+    (1, 2, 7, 16, 16, "f32"),
+    (2, 1, 33, 64, 64, "f32"),
+    (1, 1, 100, 64, 40, "f32"),
+    (1, 1, 1, 64, 256, "bf16"),
+    (2, 2, 31, 64, 64, "bf16"),
+    (1, 3, 257, 64, 256, "bf16"),
+    (1, 1, 1000, 64, 128, "bf16"),
+    (2, 1, 130, 16, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("kind", ["trig", "relu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=[f"{s[0]}x{s[1]}x{s[2]}_d{s[3]}_m{s[4]}_{s[5]}" for s in SMALL])
+def test_small_full(shape, kind, causal):
+    B, H, L, d, m, dtype = shape
+    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=L)
+    ref = O.favor_attention(q, k, v, W, kind, causal)
+    for path in _paths(B, H, L, d, m, dtype, kind, causal):
+        got = _run(dev, kind, causal, path)
+        ok = np.isfinite(ref).all(axis=-1)
+        if kind == "relu":
+            # rows with phi(q).phi(K) == 0 are 0/0 on both sides
+            assert np.array_equal(ok, np.isfinite(got).all(axis=-1)), path
+            got, ref_ = got * ok[..., None], np.where(ok[..., None], ref, 0.0)
+        else:
+            assert ok.all()
+            ref_ = ref
+        err = slice_rel_err(np.nan_to_num(got), ref_)
+        print(f"[{path}] {shape} {kind} causal={causal} rel={err:.3e}", flush=True)
+        assert err <= TOL[dtype], (path, err)
+
+
+def test_config1_fp32():
+    w = I.WORKLOADS["c1"]
+    dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype)
+    ref = O.favor_attention(q, k, v, W, w.kind, w.causal)
+    for path in _paths(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal):
+        err = slice_rel_err(_run(dev, w.kind, w.causal, path), ref)
+        print(f"[{path}] c1 rel={err:.3e}", flush=True)
+        assert err <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["c2_trig", "c2_relu"])
+def test_config2_full(name):
+    w = I.WORKLOADS[name]
+    dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype)
+    ref = O.favor_attention(q, k, v, W, w.kind, w.causal, workers=O.default_workers())
+    for path in _paths(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal):
+        err = slice_rel_err(_run(dev, w.kind, w.causal, path), ref)
+        print(f"[{path}] {name} rel={err:.3e}", flush=True)
+        assert err <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["c3_causal", "head", "c4_bidir", "c4_causal"])
+def test_full_size_sampled_rows(name):
+    w = I.WORKLOADS[name]
+    dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype, norm_shells=w.norm_shells)
+    rows = I.sample_rows(w.L, 256, seed=0)
+    ref = O.favor_rows(q, k, v, W, w.kind, w.causal, rows)
+    for path in _paths(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal):
+        got = _run(dev, w.kind, w.causal, path)[..., rows, :]
+        err = slice_rel_err(got, ref)
+        print(f"[{path}] {name} sampled rel={err:.3e}", flush=True)
+        assert err <= 2e-2
+
+
+def test_causal_matches_masked_form_c3_rows():
+    # config 3 is also checked against the explicitly masked quadratic form
+    w = I.WORKLOADS["c3_causal"]
+    dev, (q, k, v), W = problem(1, 2, w.L, w.d, w.m, w.dtype)
+    rows = np.array([0, 1, 2, 3, 511, 512, 1023, 2047, 4094, 4095])
+    ref = O.favor_quadratic_rows(q, k, v, W, "trig", True, rows)
+    for path in _paths(1, 2, w.L, w.d, w.m, w.dtype, "trig", True):
+        got = _run(dev, "trig", True, path)[..., rows, :]
+        assert slice_rel_err(got, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic(causal):
+    dev, _, _ = problem(2, 4, 2048, 64, 256, "bf16", seed=11)
+    for path in _paths(2, 4, 2048, 64, 256, "bf16", "trig", causal):
+        a = F.favor_attention(*dev, kind="trig", causal=causal, path=path)
+        b = F.favor_attention(*dev, kind="trig", causal=causal, path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), path
+
+
+def test_workspace_contents_ignored():
+    dev, (q, k, v), W = problem(1, 2, 300, 64, 256, "bf16", seed=3)
+    ref = O.favor_attention(q, k, v, W, "trig", True)
+    for path in _paths(1, 2, 300, 64, 256, "bf16", "trig", True):
+        need = F.favor_attention_workspace_bytes(1, 2, 300, 64, 256, "bf16", "trig", True, path)
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage
+        out = F.favor_attention(*dev, kind="trig", causal=True, path=path, workspace=ws)
+        torch.cuda.synchronize()
+        assert slice_rel_err(from_device(out), ref) <= 2e-2
+
+
+def test_nonfinite_input_propagates():
+    dev, _, _ = problem(1, 1, 64, 64, 256, "bf16", seed=4)
+    q, k, v, w = dev
+    v = v.clone()
+    v[0, 0, 5, 3] = float("nan")
+    for path in _paths(1, 1, 64, 64, 256, "bf16", "trig", False):
+        out = F.favor_attention(q, k, v, w, kind="trig", path=path)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[0, 0, :, 3]).all()
+
+
+def test_profile_reports_kernels():
+    dev, _, _ = problem(1, 2, 512, 64, 256, "bf16")
+    for path in _paths(1, 2, 512, 64, 256, "bf16", "trig", False):
+        phases = F.favor_profile_attention(*dev, kind="trig", path=path, iters=3)
+        assert phases and all(ms > 0 for _, ms in phases)
