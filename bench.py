@@ -1,0 +1,291 @@
+"""FAVOR attention throughput on one MI355X.
+
+One step = one favor_attention call (scale, project, feature map,
+key-side contraction, query readout, normalise and store) over the
+headline workload: B=4, H=8, L=4096, d=64, m=256, bf16 inputs, trig
+(sin/cos) features, bidirectional.  Inputs are synthetic (seeded
+N(0,1) * d^-1/4) and resident in HBM before timing starts.
+
+Prints one JSON line:
+  value     = tokens x heads per second over the timed steps
+  roofline  = the dominant kernel's algorithmic rate against the MI355X
+              peak of the unit that bounds it, timed with HIP events on
+              the launch stream inside this run
+  cpu_baseline = the float64 CPU oracle on the same workload, host cores
+  extra     = the other workloads (causal, long sequence, ReLU, the
+              masked-LM block) timed the same way, for context
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--no-extra] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FAVOR attention (tokens x heads)/s at L=4096,d=64,m=256; % of MFMA/HBM roofline"
+UNIT = "tokens*heads/s"
+
+# MI355X published peaks
+PEAK_BF16_MFMA_TFLOPS = 2516.6   # dense, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def feature_width(m, kind):
+    return 2 * m if kind == "trig" else m
+
+
+def kernel_work(name: str, B, H, L, d, m, kind, esz=2):
+    """(algorithmic flops, algorithmic HBM bytes) of one launch of a kernel.
+
+    Per token-head (tok.h): projection 2dm flops per tensor, contraction
+    2F(d+1) flops on the key side, readout 2F(d+1) flops on the query
+    side; bytes: read Q, K, V and write out, d*esz each."""
+    F = feature_width(m, kind)
+    T = B * H * L
+    proj = 2 * d * m
+    con = 2 * F * (d + 1)
+    if name.endswith("state") or "kv_state" in name:
+        return T * (proj + con), T * 2 * d * esz
+    if "readout" in name:
+        if "causal" in name:
+            return T * 2 * (proj + con), T * 4 * d * esz
+        return T * (proj + con), T * 2 * d * esz
+    return 0.0, 0.0
+
+
+def path_total_work(B, H, L, d, m, kind, esz=2):
+    F = feature_width(m, kind)
+    T = B * H * L
+    return T * (4 * d * m + 4 * F * (d + 1)), T * 4 * d * esz
+
+
+def sha256_of(path):
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; otherwise None."""
+    fn = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(fn):
+        return None
+    try:
+        rec = json.load(open(fn))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "linear_kernelized_attention_amd", "csrc", ent["source"])
+    if not os.path.exists(src) or sha256_of(src) != ent.get("source_sha256"):
+        return None
+    return float(ent["bytes_per_launch"])
+
+
+def upload(ai, dtype):
+    import torch
+    if dtype == "f32":
+        return [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (ai.q, ai.k, ai.v)]
+    return [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+            for x in (ai.q, ai.k, ai.v)]
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_attention(F, I, w, steps, warmup, path="auto"):
+    import torch
+    ai, dr = I.workload_inputs(w)
+    q, k, v = upload(ai, w.dtype)
+    omega = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, w.m)).cuda()
+    out = torch.empty_like(q)
+    need = F.favor_attention_workspace_bytes(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal, path)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: F.favor_attention(q, k, v, omega, kind=w.kind, causal=w.causal, path=path, out=out,
+                                   workspace=ws)
+    sec = time_calls(fn, steps, warmup)
+    phases = F.favor_profile_attention(q, k, v, omega, kind=w.kind, causal=w.causal, path=path,
+                                       iters=max(steps, 20), out=out, workspace=ws)
+    resolved = F.favor_attention_resolve_path(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal, path)
+    return sec, phases, resolved
+
+
+def bench_block(F, I, steps, warmup):
+    import torch
+    cfg = I.BLOCK_WORKLOAD
+    b = I.block_inputs(B=cfg["B"], L=cfg["L"], E=cfg["E"], H=cfg["H"], seed=0)
+    dr = I.omega_draws(cfg["m"], cfg["d"], seed=0)
+    omega = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, cfg["m"])).cuda()
+    dev = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+           for x in (b.embed, b.wq, b.wk, b.wv, b.wo)]
+    ids = torch.from_numpy(b.ids).cuda()
+    fn = lambda: F.favor_performer_block(ids, *dev, omega, heads=cfg["H"], kind=cfg["kind"])
+    return time_calls(fn, steps, warmup)
+
+
+def cpu_baseline(I, w, min_seconds=10.0):
+    """The float64 oracle, as it stands, on the whole headline workload
+    (repeated until min_seconds of wall time), one worker thread per core."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import favor_oracle as O
+    ai, dr = I.workload_inputs(w)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, w.m)
+    cores = O.default_workers()
+    workers = max(1, min(cores, w.B * w.H))
+    reps = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            O.favor_attention(ai.q64, ai.k64, ai.v64, W, w.kind, w.causal, workers=workers)
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    el = time.perf_counter() - t0
+    return {
+        "value": reps * w.tokens_x_heads / el,
+        "unit": UNIT,
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"full workload B={w.B} H={w.H} L={w.L} d={w.d} m={w.m} {w.kind} "
+                  f"{'causal' if w.causal else 'bidirectional'}, float64 numpy, {reps} pass(es) "
+                  f"in {el:.1f} s, one worker per head, BLAS at 1 thread",
+    }
+
+
+def calibrate_copy(steps=10, mib=1024):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return mib * (1 << 20)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--path", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_kernelized_attention_amd as F
+    from linear_kernelized_attention_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        nbytes = calibrate_copy()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes}), flush=True)
+
+    w = I.WORKLOADS["head"]
+    sec, phases, resolved = bench_attention(F, I, w, args.steps, args.warmup, args.path)
+    value = w.tokens_x_heads / sec
+
+    # dominant kernel: the longest phase of one call
+    name, ms = max(phases, key=lambda p: p[1])
+    flops, nbytes = kernel_work(name, w.B, w.H, w.L, w.d, w.m, w.kind)
+    mfma = resolved == "mfma"
+    if mfma:
+        achieved = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA_TFLOPS}
+    else:
+        achieved = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS}
+    roof["traffic"] = load_traffic(name)
+    roof["kernel"] = name
+    roof["kernel_ms"] = ms
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["algorithmic_bytes_per_launch"] = nbytes
+    tot_flops, tot_bytes = path_total_work(w.B, w.H, w.L, w.d, w.m, w.kind)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1)*d^-1/4 Q,K,V; ORF Omega (4 blocks of 64x64)",
+        "config": {"workload": "favor_attention bidirectional trig", "B": w.B, "H": w.H, "L": w.L,
+                   "d": w.d, "m": w.m, "kind": w.kind, "causal": w.causal, "path": resolved},
+        "roofline": roof,
+        "step_mfma_frac": tot_flops / sec / 1e12 / PEAK_BF16_MFMA_TFLOPS,
+        "step_hbm_frac": tot_bytes / sec / 1e9 / PEAK_HBM_GBS,
+        "phases_ms": {n: t for n, t in phases},
+    }
+
+    if not args.no_extra:
+        extra = {}
+        steps = max(10, args.steps // 4)
+        for key in ("c3_causal", "c2_trig", "c2_relu", "c4_bidir", "c4_causal", "c1"):
+            wk = I.WORKLOADS[key]
+            s, ph, rp = bench_attention(F, I, wk, steps, max(3, args.warmup // 4), "auto")
+            fl, by = path_total_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind, 4 if wk.dtype == "f32" else 2)
+            extra[key] = {"us_per_call": s * 1e6, "tokens_x_heads_per_s": wk.tokens_x_heads / s,
+                          "path": rp, "mfma_frac": fl / s / 1e12 / PEAK_BF16_MFMA_TFLOPS,
+                          "hbm_frac": by / s / 1e9 / PEAK_HBM_GBS,
+                          "phases_ms": {n: t for n, t in ph}}
+        sb = bench_block(F, I, steps, 3)
+        extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": 2 * 4096 / sb}
+        rec["extra"] = extra
+
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(I, w)
+    else:
+        rec["cpu_baseline"] = None
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -39,12 +39,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* ids, const uint16
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int APAD = 8, BPAD = 8;  // bf16 elements of padding per LDS row
 
-__device__ inline uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// round to nearest even (lowers to v_cvt_pk_bf16_f32)
+__device__ inline uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 struct GemmArgs {
   const uint16_t* X;

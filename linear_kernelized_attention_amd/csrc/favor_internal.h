@@ -38,7 +38,7 @@ struct PhaseHook {
 
 inline void phase_begin(PhaseHook* h, hipStream_t s, const char* name) {
   if (!h || h->n >= h->max_phases) return;
-  hipEventRecord(h->ev[2 * h->n], s);
+  (void)hipEventRecord(h->ev[2 * h->n], s);
   if (h->names) {
     char* dst = h->names + 48 * h->n;
     int i = 0;
@@ -49,7 +49,7 @@ inline void phase_begin(PhaseHook* h, hipStream_t s, const char* name) {
 
 inline void phase_end(PhaseHook* h, hipStream_t s) {
   if (!h || h->n >= h->max_phases) return;
-  hipEventRecord(h->ev[2 * h->n + 1], s);
+  (void)hipEventRecord(h->ev[2 * h->n + 1], s);
   ++h->n;
 }
 

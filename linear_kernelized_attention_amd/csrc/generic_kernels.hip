@@ -65,13 +65,7 @@ template <>
 __device__ inline void st<float>(float* p, size_t i, float x) { p[i] = x; }
 template <>
 __device__ inline void st<uint16_t>(uint16_t* p, size_t i, float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
-    p[i] = (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-    return;
-  }
-  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
-  p[i] = (uint16_t)(u >> 16);
+  p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }
 
 // Global feature index of local feature fl in the chunk starting at row r0
