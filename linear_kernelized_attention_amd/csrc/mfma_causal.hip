@@ -1,0 +1,445 @@
+// Causal FAVOR on MFMA for gfx950 (bf16, d = 64, m a multiple of 32 up to
+// 256): out_i = phi(q_i)^T S_i / phi(q_i)^T z_i with the inclusive prefix
+// sums S_i = sum_{j <= i} phi(k_j) v_j^T, z_i = sum_{j <= i} phi(k_j)
+// (FAVOR+ blog page "用随机特征“骗”过 softmax，Transformer 注意力也能跑成线性？",
+// section 核心机制：FAVOR+, causal variant).
+//
+// Three kernels per call:
+//  kv_state : the per-segment key/value state sum_{t in seg} phi(k_t) [c v | c]
+//             (the same kernel as the bidirectional path, one split per
+//             segment), bf16 partials.
+//  scan     : exclusive prefix over segments in float32: the state every
+//             segment starts from.
+//  causal   : one block per (head, segment) walks the segment in chunks of
+//             32 tokens.  Wave w owns Omega rows [32 w, 32 w + 32) and keeps
+//             the float32 running state of its features in registers.  For a
+//             chunk it computes, over its own features only,
+//               part_w = S_prev,w^T phi_Q,w^T + V'^T (mask . phi_K,w phi_Q,w^T)
+//             (the masked intra-chunk scores are linear in the features, so
+//             feature-slice partials add up exactly), then updates its state
+//             S_w += phi_K,w^T V'.  The partial outputs of all waves are summed
+//             through LDS in float32 and normalised (row 64 of the value tile
+//             carries c_t, so row 64 of out^T is the denominator).
+//  phi(K) is needed with tokens along the fragment (state update) and with
+//  features along the fragment (scores); each wave transposes its own bf16
+//  feature tile through a private LDS region.
+#include "mfma_common.h"
+
+namespace favor {
+namespace mfma {
+namespace {
+
+constexpr int CT = 32;           // tokens per causal chunk
+constexpr int CROW = CT + 8;     // padded LDS row of the chunk's transposed values
+constexpr int RED_FLOATS = 5 * 2 * 64 * 4;   // one wave's partial out^T (80 x 32)
+
+// Transposed value tile of a chunk: slot s of row `row`, 16-byte groups of 8
+// slots XOR-swizzled by (row / 8) % 4.
+__device__ inline int ct_index(int row, int s) {
+  return row * CROW + (((s >> 3) ^ ((row >> 3) & 3)) << 3) + (s & 7);
+}
+
+// ------------------------------------------------------------------ scan
+// start[seg] = sum_{s < seg} part[s] over [seg][head][F][72], float32, in a
+// fixed order; one thread per 8 consecutive elements.
+__global__ __launch_bounds__(256) void scan_kernel(const uint16_t* __restrict__ part,
+                                                   float* __restrict__ start, int n_seg,
+                                                   long long per_seg8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_seg8) return;
+  float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sg = 0; sg < n_seg; ++sg) {
+    const u32x4 v = *(const u32x4*)(part + ((size_t)sg * per_seg8 + i) * 8);
+    float4* dst = (float4*)(start + ((size_t)sg * per_seg8 + i) * 8);
+    dst[0] = make_float4(run[0], run[1], run[2], run[3]);
+    dst[1] = make_float4(run[4], run[5], run[6], run[7]);
+    const uint16_t* h = (const uint16_t*)&v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) run[e] += bf16_to_f32(h[e]);
+  }
+}
+
+// ---------------------------------------------------------------- causal
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void causal_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ Omega,
+    const float* __restrict__ start, uint16_t* __restrict__ out, int L, int seg_len, int n_seg,
+    long long BH, float omega_scale, float knorm_scale) {
+  constexpr bool TRIG = KIND == KIND_TRIG;
+  constexpr int M = NW * 32;
+  constexpr int F = TRIG ? 2 * M : M;
+  constexpr int FT = TRIG ? 4 : 2;    // feature tiles of 16 per wave
+  constexpr int KS = TRIG ? 2 : 1;    // 32-feature k-steps per wave
+  constexpr int NT = NW * 64;
+  constexpr int NQT = CT * 8;         // query staging tasks (token, 8 columns)
+  constexpr int NKV = CT / 2 * 8;     // key/value staging tasks (token pair, 8 columns)
+  constexpr int NTASK = NQT + NKV;
+  constexpr int CH = (NTASK + NT - 1) / NT;
+
+  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
+  const long long bh = lb / n_seg;
+  const int seg = (int)(lb % n_seg);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const long long seg0 = (long long)seg * seg_len;
+  const long long seg1 = min((long long)L, seg0 + seg_len);
+  const size_t head = (size_t)bh * L * D;
+
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][CT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][CT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][NCOL * CROW];
+  // per wave: the transposed phi(K) tile, later reused for the partial out^T
+  __shared__ __attribute__((aligned(16))) float Red[NW][RED_FLOATS];
+  // per wave: its Omega~ fragments (2 row tiles x 2 column halves)
+  __shared__ __attribute__((aligned(16))) uint16_t Om[NW][4 * 512];
+
+  for (int i = tid; i < 2 * (NCOL - SCOL) * CROW; i += NT) {
+    const int b = i / ((NCOL - SCOL) * CROW), e = i % ((NCOL - SCOL) * CROW);
+    Vt[b][SCOL * CROW + e] = 0;
+  }
+
+#pragma unroll
+  for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      *(bf16x8*)&Om[w][((ot * 2 + kk) * 64 + lane) * 8] =
+          omega_frag(Omega, 32 * w + 16 * ot, kk, lane, omega_scale);
+  auto om = [&](int ot, int kk) { return *(const bf16x8*)&Om[w][((ot * 2 + kk) * 64 + lane) * 8]; };
+
+  // running state of this wave's features: S_w[f][col] as MFMA C fragments
+  floatx4 acc_s[FT][5];
+  {
+    const float* st = start + ((size_t)seg * BH + bh) * (size_t)F * PCOL;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const int row0 = (TRIG ? (ft >> 1) * M : 0) + 32 * w + 16 * (ft & 1) + 4 * g;
+#pragma unroll
+      for (int n = 0; n < 5; ++n) {
+        const int col = 16 * n + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc_s[ft][n][r] = col < SCOL ? st[(size_t)(row0 + r) * PCOL + col] : 0.f;
+      }
+    }
+  }
+
+  // raw chunk data of this thread's staging tasks: a query task keeps one
+  // 16-byte chunk in d[0]; a key/value task keeps k(t), k(t+1), v(t), v(t+1)
+  struct Raw {
+    u32x4 d[CH][4];
+  };
+  Raw ra;
+  auto fetch = [&](Raw& r, long long t0) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int task = tid + k * NT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.d[k][e] = u32x4{0u, 0u, 0u, 0u};
+      if (task < NQT) {
+        const long long tok = t0 + (task >> 3);
+        if (tok < seg1) r.d[k][0] = *(const u32x4*)(Q + head + (size_t)tok * D + (task & 7) * 8);
+      } else if (task < NTASK) {
+        const int kv = task - NQT;
+        const int t = pair_token(kv >> 3), c8 = kv & 7;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const long long tok = t0 + t + h;
+          if (tok < seg1) {
+            r.d[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
+            r.d[k][2 + h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
+          }
+        }
+      }
+    }
+  };
+  auto stage = [&](const Raw& r, int buf, long long t0) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int task = tid + k * NT;
+      const bool kvtask = task >= NQT && task < NTASK;
+      float ct[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t* kv = (const uint16_t*)&r.d[k][h];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = kvtask ? bf16_to_f32(kv[i]) : 0.f;
+          ss = fmaf(x, x, ss);
+        }
+        ss = octet_sum(ss);
+        ct[h] = TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f;
+      }
+      if (task < NQT) {
+        *(u32x4*)&Qs[buf][(task >> 3) * KROW + (task & 7) * 8] = r.d[k][0];
+      } else if (task < NTASK) {
+        const int kv = task - NQT;
+        const int q = kv >> 3, c8 = kv & 7;
+        const int t = pair_token(q);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (t0 + t + h >= seg1) ct[h] = 0.f;
+        *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = r.d[k][0];
+        *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = r.d[k][1];
+        const uint16_t* v0 = (const uint16_t*)&r.d[k][2];
+        const uint16_t* v1 = (const uint16_t*)&r.d[k][3];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *(uint32_t*)&Vt[buf][ct_index(c8 * 8 + i, 2 * q)] =
+              pack2(bf16_to_f32(v0[i]) * ct[0], bf16_to_f32(v1[i]) * ct[1]);
+        if (c8 == 0) *(uint32_t*)&Vt[buf][ct_index(D, 2 * q)] = pack2(ct[0], ct[1]);
+      }
+    }
+  };
+
+  uint16_t* kt = (uint16_t*)Red[w];   // this wave's transposed phi(K) fragments
+
+  auto compute = [&](int buf) {
+    const uint16_t* qs = Qs[buf];
+    const uint16_t* ks = Ks[buf];
+    const uint16_t* vt = Vt[buf];
+    // (a) key projection P_K[ts][ot]: token 16 ts + 4 g + r, Omega row 16 ot + c
+    floatx4 PK[2][2];
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
+      const bf16x8 k0 = *(const bf16x8*)&ks[(16 * ts + c) * KROW + 8 * g];
+      const bf16x8 k1 = *(const bf16x8*)&ks[(16 * ts + c) * KROW + 32 + 8 * g];
+#pragma unroll
+      for (int ot = 0; ot < 2; ++ot) {
+        floatx4 p = {0.f, 0.f, 0.f, 0.f};
+        p = mfma16(k0, om(ot, 0), p);
+        PK[ts][ot] = mfma16(k1, om(ot, 1), p);
+      }
+    }
+    // (b) key features: fk[ft] A fragments (feature rows x token slots,
+    //     slot j = 4 ts + r <-> token 16 ts + 4 g + r); (c) the same values,
+    //     transposed into this wave's LDS region as the A fragments of the
+    //     scores (token rows x features): fragment (ts, ks), lane
+    //     16 (c / 4) + 4 g + r, slot 4 ot + c % 4.
+    bf16x8 fk[FT];
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot) {
+      float sv[8], cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (TRIG) sincos_rev(PK[j >> 2][ot][j & 3], &sv[j], &cv[j]);
+        else sv[j] = fmaxf(PK[j >> 2][ot][j & 3], 0.f);
+      }
+      fk[ot] = pack8(sv);
+      if (TRIG) fk[2 + ot] = pack8(cv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ts = j >> 2, r = j & 3;
+        const int dl = 16 * (c >> 2) + 4 * g + r, ds = 4 * ot + (c & 3);
+        kt[((ts * KS + 0) * 64 + dl) * 8 + ds] = bf16_bits(sv[j]);
+        if (TRIG) kt[((ts * KS + 1) * 64 + dl) * 8 + ds] = bf16_bits(cv[j]);
+      }
+    }
+    // (d) query projection P_Q^T[ot][nt]: Omega row 16 ot + 4 g + r, token 16 nt + c
+    floatx4 PQ[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16x8 q0 = *(const bf16x8*)&qs[(16 * nt + c) * KROW + 8 * g];
+      const bf16x8 q1 = *(const bf16x8*)&qs[(16 * nt + c) * KROW + 32 + 8 * g];
+#pragma unroll
+      for (int ot = 0; ot < 2; ++ot) {
+        floatx4 p = {0.f, 0.f, 0.f, 0.f};
+        p = mfma16(om(ot, 0), q0, p);
+        PQ[ot][nt] = mfma16(om(ot, 1), q1, p);
+      }
+    }
+    // (e) query features: B fragments (features x tokens), slot j <-> row
+    //     16 (j / 4) + 4 g + j % 4 of this wave's 32 rows
+    bf16x8 bq[KS][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float sv[8], cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (TRIG) sincos_rev(PQ[j >> 2][nt][j & 3], &sv[j], &cv[j]);
+        else sv[j] = fmaxf(PQ[j >> 2][nt][j & 3], 0.f);
+      }
+      bq[0][nt] = pack8(sv);
+      if (TRIG) bq[KS - 1][nt] = pack8(cv);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // (f) partial scores over this wave's features, transposed:
+    //     Sc^T[mk][nq]: key token 16 mk + 4 g + r, query token 16 nq + c
+    floatx4 sc[2][2];
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk) {
+      bf16x8 ka[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ka[s] = *(const bf16x8*)&kt[((mk * KS + s) * 64 + lane) * 8];
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        floatx4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) p = mfma16(ka[s], bq[s][nq], p);
+        sc[mk][nq] = p;
+      }
+    }
+    // (g) causal mask (key <= query, diagonal kept) -> B fragments whose slot
+    //     j <-> key token 16 (j / 4) + 4 g + j % 4, the value tile's order
+    bf16x8 bs[2];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kt_tok = 16 * (j >> 2) + 4 * g + (j & 3), q_tok = 16 * nq + c;
+        v[j] = kt_tok <= q_tok ? sc[j >> 2][nq][j & 3] : 0.f;
+      }
+      bs[nq] = pack8(v);
+    }
+    // (h) partial out^T = S_prev,w^T phi_Q,w^T + V'^T (mask . Sc^T), one
+    //     16-token query half at a time, written to this wave's LDS region
+    //     (the phi(K) tile there is dead once the scores are formed)
+    bf16x8 vf[5];
+#pragma unroll
+    for (int mt = 0; mt < 5; ++mt) {
+      const int row = 16 * mt + c;
+      vf[mt] = *(const bf16x8*)&vt[row * CROW + ((g ^ ((row >> 3) & 3)) << 3)];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      floatx4 ao[5];
+#pragma unroll
+      for (int mt = 0; mt < 5; ++mt) ao[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 5; ++mt) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = acc_s[KS == 2 ? 2 * s + (j >> 2) : (j >> 2)][mt][j & 3];
+          ao[mt] = mfma16(pack8(v), bq[s][nq], ao[mt]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 5; ++mt) {
+        ao[mt] = mfma16(vf[mt], bs[nq], ao[mt]);
+        *(floatx4*)&Red[w][((mt * 2 + nq) * 64 + lane) * 4] = ao[mt];
+      }
+    }
+    // (i) state update S_w += phi_K,w^T V'
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int n = 0; n < 5; ++n) acc_s[ft][n] = mfma16(fk[ft], vf[n], acc_s[ft][n]);
+  };
+
+  // Sum the waves' partial out^T tiles (mt < 4) and normalise by row 64.
+  auto reduce_store = [&](long long t0) {
+    for (int tile = w; tile < 8; tile += NW) {
+      const int mt = tile >> 1, nq = tile & 1;
+      floatx4 num = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        num += *(const floatx4*)&Red[ww][((mt * 2 + nq) * 64 + lane) * 4];
+        den += Red[ww][((4 * 2 + nq) * 64 + c) * 4];
+      }
+      const long long tok = t0 + 16 * nq + c;
+      if (tok < seg1) {
+        const float inv = 1.0f / den;
+        u32x2 o;
+        o[0] = pack2(num[0] * inv, num[1] * inv);
+        o[1] = pack2(num[2] * inv, num[3] * inv);
+        *(u32x2*)(out + head + (size_t)tok * D + 16 * mt + 4 * g) = o;
+      }
+    }
+  };
+
+  const int n_chunks = (int)((seg1 - seg0 + CT - 1) / CT);
+  fetch(ra, seg0);
+  stage(ra, 0, seg0);
+  __syncthreads();
+  for (int i = 0; i < n_chunks; ++i) {
+    const int buf = i & 1;
+    const long long t0 = seg0 + (long long)i * CT;
+    const bool more = i + 1 < n_chunks;
+    if (more) fetch(ra, t0 + CT);
+    compute(buf);
+    if (more) stage(ra, buf ^ 1, t0 + CT);
+    __syncthreads();
+    reduce_store(t0);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- host
+struct CausalPlan {
+  Plan keys;
+  size_t start_bytes;
+};
+
+CausalPlan plan_causal(const Problem& p) {
+  CausalPlan cp;
+  int rows = 128;
+  while (rows > 16 && p.m % rows) rows -= 16;
+  const int n_fpart = p.m / rows;
+  // one causal block per (head, segment); about 256 of them
+  cp.keys = plan_keys(p, 256LL * n_fpart, TK);
+  cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * p.F * PCOL * sizeof(float), 256);
+  return cp;
+}
+
+template <int KIND, int NW>
+void launch_causal(const Problem& p, const Buffers& b, const CausalPlan& cp, const float* start,
+                   hipStream_t s, float oscale) {
+  hipLaunchKernelGGL((causal_kernel<KIND, NW>), dim3((unsigned)((long long)cp.keys.n_split * p.BH)),
+                     dim3(NW * 64), 0, s, (const uint16_t*)b.q, (const uint16_t*)b.k,
+                     (const uint16_t*)b.v, b.omega, start, (uint16_t*)b.out, p.L, cp.keys.seg_len,
+                     cp.keys.n_split, p.BH, oscale, 1.0f / sqrtf((float)D));
+}
+
+template <int KIND>
+hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
+  const CausalPlan cp = plan_causal(p);
+  const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
+  float* start = (float*)((char*)b.ws + cp.keys.part_bytes);
+
+  phase_begin(hook, s, "mfma_kv_state");
+  launch_kv_nw<KIND>(p, b, cp.keys, s, oscale);
+  phase_end(hook, s);
+
+  const long long per_seg8 = p.BH * (long long)p.F * PCOL / 8;
+  phase_begin(hook, s, "mfma_state_scan");
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s,
+                     (const uint16_t*)b.ws, start, cp.keys.n_split, per_seg8);
+  phase_end(hook, s);
+
+  phase_begin(hook, s, "mfma_causal_chunks");
+  switch (p.m / 32) {
+    case 1: launch_causal<KIND, 1>(p, b, cp, start, s, oscale); break;
+    case 2: launch_causal<KIND, 2>(p, b, cp, start, s, oscale); break;
+    case 3: launch_causal<KIND, 3>(p, b, cp, start, s, oscale); break;
+    case 4: launch_causal<KIND, 4>(p, b, cp, start, s, oscale); break;
+    case 5: launch_causal<KIND, 5>(p, b, cp, start, s, oscale); break;
+    case 6: launch_causal<KIND, 6>(p, b, cp, start, s, oscale); break;
+    case 7: launch_causal<KIND, 7>(p, b, cp, start, s, oscale); break;
+    default: launch_causal<KIND, 8>(p, b, cp, start, s, oscale); break;
+  }
+  phase_end(hook, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t causal_workspace_bytes(const Problem& p) {
+  const CausalPlan cp = plan_causal(p);
+  return cp.keys.part_bytes + cp.start_bytes;
+}
+
+hipError_t run_causal(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
+  if (p.kind == KIND_TRIG) return run_causal_kind<KIND_TRIG>(p, b, s, hook);
+  return run_causal_kind<KIND_RELU>(p, b, s, hook);
+}
+
+}  // namespace mfma
+}  // namespace favor

@@ -33,290 +33,11 @@
 //  readout  : per wave 64 query tokens: P^T = Omega~ Q~^T (rows x tokens)
 //             -> features -> out^T = S^T phi(Q)^T; the fifth row tile yields
 //             the denominator for every token; out = num / den, bf16 stores.
-#include "favor_internal.h"
+#include "mfma_common.h"
 
 namespace favor {
 namespace mfma {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-
-constexpr int D = 64;         // head dimension
-constexpr int NCOL = 80;      // value columns incl. the z column, padded to 5 x 16
-constexpr int SCOL = D + 1;   // columns of a state (values and z)
-constexpr int PCOL = 72;      // padded partial row (16-byte multiple)
-constexpr int TT = 32;        // tokens per key tile
-constexpr int KPAD = 8;       // bf16 padding per LDS row
-constexpr int VPAD = 8;
-constexpr int QW = 64;        // query tokens per wave in the readout
-constexpr float INV_2PI = 0.15915494309189535f;
-
-__device__ inline floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// float -> bf16 with round-to-nearest-even: the cast lowers to the gfx950
-// v_cvt_pk_bf16_f32 instruction.
-__device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-
-__device__ inline uint32_t pack2(float lo, float hi) {
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-  bf16x2 v;
-  v[0] = (__bf16)lo;
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ inline bf16x8 pack8(const float* v) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)v[j];
-  return r;
-}
-
-// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8), each with its own L2.  Renumber blocks so that consecutive logical
-// blocks -- the blocks of one head, which read the same keys, values and
-// state -- run on the same XCD and share its L2.
-__device__ inline long long xcd_logical(long long b, long long total) {
-  if (total % 8) return b;
-  return (b % 8) * (total / 8) + b / 8;
-}
-
-// sin/cos of 2*pi*x via the hardware units, after exact range reduction.
-__device__ inline void sincos_rev(float x, float* s, float* c) {
-  const float f = __builtin_amdgcn_fractf(x);
-  *s = __builtin_amdgcn_sinf(f);
-  *c = __builtin_amdgcn_cosf(f);
-}
-
-// Position of token t (0..31) of a key tile inside the permuted K dimension
-// of the contraction: the projection's C fragment of token sub-tile ts = t/16
-// puts token 16 ts + 4 g + r in lane group g, register r, and the A fragment
-// slot j = 4 ts + r of group g is logical k = 8 g + j.
-__device__ inline int key_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
-
-// Load Omega rows [row0, row0 + 16) x columns [32 kk, 32 kk + 32) as the
-// fragment lane l needs (row row0 + c, columns 32 kk + 8 g + j), scaled.
-__device__ inline bf16x8 omega_frag(const float* Omega, int row0, int kk, int lane, float scale) {
-  const int c = lane & 15, g = lane >> 4;
-  const float4* p = (const float4*)(Omega + (size_t)(row0 + c) * D + 32 * kk + 8 * g);
-  const float4 a = p[0], b = p[1];
-  float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
-                b.x * scale, b.y * scale, b.z * scale, b.w * scale};
-  return pack8(v);
-}
-
-// --------------------------------------------------------------- kv_state
-// First token of the token pair that occupies slots 2q, 2q + 1 of a key
-// tile; slot s of k-step s / 32 holds token 32 (s / 32) + key_slot^-1(s % 32).
-__device__ inline int pair_token(int q) {
-  const int s = 2 * q, s5 = s & 31;
-  return 32 * (s >> 5) + 16 * ((s5 >> 2) & 1) + 4 * (s5 >> 3) + (s5 & 3);
-}
-
-constexpr int TK = 128;           // tokens per key tile (4 contraction k-steps)
-constexpr int VROW = TK + 8;      // padded LDS row of the transposed values
-constexpr int KROW = D + 8;       // padded LDS row of the keys
-
-// Element offset of (value column `row`, token slot s) in the transposed
-// value tile: 16-byte groups of 8 slots are XOR-swizzled by row / 8 so that
-// both the staging writes and the fragment reads avoid bank conflicts.
-__device__ inline int vt_index(int row, int s) {
-  return row * VROW + (((s >> 3) ^ ((row >> 3) & 7)) << 3) + (s & 7);
-}
-
-// Sum over the 8 lanes of an aligned lane octet (DPP, no LDS traffic).
-__device__ inline float octet_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
-  return x;
-}
-
-// Block = (token split, feature part, head); NW waves, wave w owns the 16
-// Omega rows r0 = part * 16 NW + 16 w .. +15.  Writes a bf16 partial
-// [split][head][F][65] for its rows (trig: sin rows r, cos rows M + r).
-template <int KIND, int NW>
-__global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V,
-                                                           const float* __restrict__ Omega,
-                                                           uint16_t* __restrict__ part, int L,
-                                                           int M, int n_fpart, int seg_len,
-                                                           long long BH, float omega_scale,
-                                                           float knorm_scale) {
-  constexpr bool TRIG = KIND == KIND_TRIG;
-  constexpr int FT = TRIG ? 2 : 1;      // feature tiles per wave (sin, cos)
-  constexpr int NT = NW * 64;
-  constexpr int NTASK = TK / 2 * 8;     // (token pair, 8-column chunk) tasks
-  constexpr int CH = (NTASK + NT - 1) / NT;
-  const long long nx = (long long)gridDim.x / BH;   // blocks per head
-  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  const long long bh = lb / nx;
-  const int split = (int)(lb % nx) / n_fpart, fpart = (int)(lb % nx) % n_fpart;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int F = TRIG ? 2 * M : M;
-  const int r0 = fpart * 16 * NW + 16 * w;
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][TK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][NCOL * VROW];
-
-  const long long seg0 = (long long)split * seg_len;
-  const long long seg1 = min((long long)L, seg0 + seg_len);
-  const size_t head = (size_t)bh * L * D;
-
-  for (int i = tid; i < 2 * (NCOL - SCOL) * VROW; i += NT) {
-    const int b = i / ((NCOL - SCOL) * VROW), e = i % ((NCOL - SCOL) * VROW);
-    Vt[b][SCOL * VROW + e] = 0;
-  }
-  const bf16x8 om0 = omega_frag(Omega, r0, 0, lane, omega_scale);
-  const bf16x8 om1 = omega_frag(Omega, r0, 1, lane, omega_scale);
-
-  floatx4 acc[FT][5];
-#pragma unroll
-  for (int f = 0; f < FT; ++f)
-#pragma unroll
-    for (int n = 0; n < 5; ++n) acc[f][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Two register sets (A, B) of raw key/value chunks give a prefetch
-  // distance of two tiles: the loads of tile i + 2 are issued before the
-  // compute of tile i, and tile i + 1 (loaded one iteration earlier) is
-  // staged after it.
-  struct Raw {
-    u32x4 k[CH][2], v[CH][2];
-  };
-  Raw ra, rb;
-  auto fetch = [&](Raw& r, long long t0) {
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int task = tid + k * NT;
-      const int t = pair_token((task >> 3) & (TK / 2 - 1)), c8 = task & 7;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const long long tok = t0 + t + h;
-        if (task < NTASK && tok < seg1) {
-          r.k[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
-          r.v[k][h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
-        } else {
-          r.k[k][h] = u32x4{0u, 0u, 0u, 0u};
-          r.v[k][h] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  auto stage = [&](const Raw& r, int buf, long long t0) {
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int task = tid + k * NT;
-      const int q = (task >> 3) & (TK / 2 - 1), c8 = task & 7;
-      const int t = pair_token(q);
-      float ct[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint16_t* kv = (const uint16_t*)&r.k[k][h];
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x = bf16_to_f32(kv[i]);
-          ss = fmaf(x, x, ss);
-        }
-        ss = octet_sum(ss);
-        ct[h] = (t0 + t + h < seg1) ? (TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f) : 0.f;
-      }
-      if (task >= NTASK) continue;
-      *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = r.k[k][0];
-      *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = r.k[k][1];
-      const uint16_t* v0 = (const uint16_t*)&r.v[k][0];
-      const uint16_t* v1 = (const uint16_t*)&r.v[k][1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint32_t*)&Vt[buf][vt_index(c8 * 8 + i, 2 * q)] =
-            pack2(bf16_to_f32(v0[i]) * ct[0], bf16_to_f32(v1[i]) * ct[1]);
-      if (c8 == 0) *(uint32_t*)&Vt[buf][vt_index(D, 2 * q)] = pack2(ct[0], ct[1]);
-    }
-  };
-  auto compute = [&](int buf) {
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vt = Vt[buf];
-#pragma unroll
-    for (int kh = 0; kh < TK / 32; ++kh) {
-      // projection of the two 16-token sub-tiles of this k-step
-      floatx4 P[2];
-#pragma unroll
-      for (int tsub = 0; tsub < 2; ++tsub) {
-        const int row = 32 * kh + 16 * tsub + c;
-        const bf16x8 k0 = *(const bf16x8*)&ks[row * KROW + 8 * g];
-        const bf16x8 k1 = *(const bf16x8*)&ks[row * KROW + 32 + 8 * g];
-        floatx4 p = {0.f, 0.f, 0.f, 0.f};
-        p = mfma16(k0, om0, p);
-        P[tsub] = mfma16(k1, om1, p);
-      }
-      bf16x8 vf[5];
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        const int row = 16 * n + c;
-        vf[n] = *(const bf16x8*)&vt[row * VROW + (((4 * kh + g) ^ ((row >> 3) & 7)) << 3)];
-      }
-      // A fragment slot j = 4 tsub + r <-> token 32 kh + 16 tsub + 4 g + r
-      bf16x8 fa[FT];
-      if (TRIG) {
-        float sv[8], cv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sincos_rev(P[j >> 2][j & 3], &sv[j], &cv[j]);
-        fa[0] = pack8(sv);
-        fa[FT - 1] = pack8(cv);
-      } else {
-        float rv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rv[j] = fmaxf(P[j >> 2][j & 3], 0.f);
-        fa[0] = pack8(rv);
-      }
-#pragma unroll
-      for (int n = 0; n < 5; ++n)
-#pragma unroll
-        for (int f = 0; f < FT; ++f) acc[f][n] = mfma16(fa[f], vf[n], acc[f][n]);
-    }
-  };
-
-  const int n_tiles = (int)((seg1 - seg0 + TK - 1) / TK);
-  fetch(ra, seg0);
-  if (n_tiles > 1) fetch(rb, seg0 + TK);
-  stage(ra, 0, seg0);
-  __syncthreads();
-  for (int i = 0; i < n_tiles; i += 2) {
-    // even step: compute tile i (buffer 0), stage tile i + 1 from B
-    if (i + 2 < n_tiles) fetch(ra, seg0 + (long long)(i + 2) * TK);
-    compute(0);
-    if (i + 1 < n_tiles) stage(rb, 1, seg0 + (long long)(i + 1) * TK);
-    __syncthreads();
-    if (i + 1 >= n_tiles) break;
-    // odd step: compute tile i + 1 (buffer 1), stage tile i + 2 from A
-    if (i + 3 < n_tiles) fetch(rb, seg0 + (long long)(i + 3) * TK);
-    compute(1);
-    if (i + 2 < n_tiles) stage(ra, 0, seg0 + (long long)(i + 2) * TK);
-    __syncthreads();
-  }
-
-  uint16_t* P0 = part + ((size_t)split * BH + bh) * (size_t)F * PCOL;
-#pragma unroll
-  for (int f = 0; f < FT; ++f) {
-    const int row0 = f * M + r0 + 4 * g;
-#pragma unroll
-    for (int n = 0; n < 5; ++n) {
-      const int col = 16 * n + c;
-      if (col < SCOL) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) P0[(size_t)(row0 + r) * PCOL + col] = bf16_bits(acc[f][n][r]);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- reduce
 // Block = (k-step, head).  k-step ks covers Omega rows 32 i .. 32 i + 31
@@ -558,61 +279,6 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------- host
 constexpr int RO_NW = 8;  // waves per readout block
 
-struct Plan {
-  int n_split, seg_len;   // token splits of the key side
-  int nw_kv, n_fpart;     // waves per kv block, feature parts per head
-  size_t part_bytes, frag_bytes, ofrag_bytes;
-};
-
-Plan plan(const Problem& p) {
-  Plan pl;
-  // a kv block owns up to 128 Omega rows (16 per wave) and all value columns
-  int rows = 128;
-  while (rows > 16 && p.m % rows) rows -= 16;
-  pl.nw_kv = rows / 16;
-  pl.n_fpart = p.m / rows;
-  const long long tiles = (p.L + TK - 1) / TK;
-  long long want = (256 + p.BH * pl.n_fpart - 1) / (p.BH * pl.n_fpart);
-  if (want < 1) want = 1;
-  if (want > tiles) want = tiles;
-  long long seg = (p.L + want - 1) / want;
-  seg = (seg + TK - 1) / TK * TK;
-  pl.seg_len = (int)seg;
-  pl.n_split = (int)((p.L + seg - 1) / seg);
-  pl.part_bytes = align_up((size_t)pl.n_split * p.BH * p.F * PCOL * sizeof(uint16_t), 256);
-  pl.frag_bytes = align_up((size_t)p.BH * (p.F / 32) * 5 * 512 * sizeof(uint16_t), 256);
-  pl.ofrag_bytes = align_up((size_t)(p.m / 16) * 2 * 512 * sizeof(uint16_t), 256);
-  return pl;
-}
-
-dim3 head_grid(long long x, long long BH) {
-  const long long y = BH < 65535 ? BH : 65535;
-  const long long z = (BH + y - 1) / y;
-  return dim3((unsigned)x, (unsigned)y, (unsigned)z);
-}
-
-template <int KIND, int NW>
-void launch_kv(const Problem& p, const Buffers& b, const Plan& pl, hipStream_t s, float oscale) {
-  hipLaunchKernelGGL((kv_state_kernel<KIND, NW>), dim3((unsigned)((long long)pl.n_split * pl.n_fpart * p.BH)),
-                     dim3(NW * 64), 0, s, (const uint16_t*)b.k, (const uint16_t*)b.v, b.omega,
-                     (uint16_t*)b.ws, p.L, p.m, pl.n_fpart, pl.seg_len, p.BH, oscale,
-                     1.0f / sqrtf((float)D));
-}
-
-template <int KIND>
-void launch_kv_nw(const Problem& p, const Buffers& b, const Plan& pl, hipStream_t s, float oscale) {
-  switch (pl.nw_kv) {
-    case 1: launch_kv<KIND, 1>(p, b, pl, s, oscale); break;
-    case 2: launch_kv<KIND, 2>(p, b, pl, s, oscale); break;
-    case 3: launch_kv<KIND, 3>(p, b, pl, s, oscale); break;
-    case 4: launch_kv<KIND, 4>(p, b, pl, s, oscale); break;
-    case 5: launch_kv<KIND, 5>(p, b, pl, s, oscale); break;
-    case 6: launch_kv<KIND, 6>(p, b, pl, s, oscale); break;
-    case 7: launch_kv<KIND, 7>(p, b, pl, s, oscale); break;
-    default: launch_kv<KIND, 8>(p, b, pl, s, oscale); break;
-  }
-}
-
 size_t readout_lds(const Problem& p) {
   return ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t);
 }
@@ -649,7 +315,7 @@ void launch_readout_m(const Problem& p, const Buffers& b, const uint16_t* frag,
 
 template <int KIND>
 hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
-  const Plan pl = plan(p);
+  const Plan pl = plan_keys(p, 256, TK);
   const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
   uint16_t* part = (uint16_t*)b.ws;
   uint16_t* frag = (uint16_t*)((char*)b.ws + pl.part_bytes);
@@ -676,17 +342,22 @@ bool lds_fits(const Problem& p) { return readout_lds(p) <= 160 * 1024; }
 
 }  // namespace
 
+size_t causal_workspace_bytes(const Problem& p);
+hipError_t run_causal(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+
 bool supports(const Problem& p) {
   return p.dtype == DT_BF16 && p.d == D && p.m % 32 == 0 && p.m >= 32 && p.m <= 256 &&
-         !p.causal && lds_fits(p);
+         lds_fits(p);
 }
 
 size_t workspace_bytes(const Problem& p) {
-  const Plan pl = plan(p);
+  if (p.causal) return causal_workspace_bytes(p);
+  const Plan pl = plan_keys(p, 256, TK);
   return pl.part_bytes + pl.frag_bytes + pl.ofrag_bytes;
 }
 
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
+  if (p.causal) return run_causal(p, b, s, hook);
   if (p.kind == KIND_TRIG) return run_kind<KIND_TRIG>(p, b, s, hook);
   return run_kind<KIND_RELU>(p, b, s, hook);
 }
