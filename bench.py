@@ -73,11 +73,17 @@ def path_total_work(B, H, L, d, m, kind, esz=2):
     return T * (4 * d * m + 4 * F * (d + 1)), T * 4 * d * esz
 
 
-def sha256_of(path):
+def sources_sha256(names):
+    """sha256 over the named kernel sources (csrc/), in order; None if any
+    is missing."""
     h = hashlib.sha256()
-    with open(path, "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()
+    for n in names:
+        p = os.path.join(ROOT, "linear_kernelized_attention_amd", "csrc", n)
+        if not os.path.exists(p):
+            return None
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest() if names else None
 
 
 def load_traffic(kernel: str):
@@ -93,8 +99,7 @@ def load_traffic(kernel: str):
     ent = rec.get("kernels", {}).get(kernel)
     if not ent:
         return None
-    src = os.path.join(ROOT, "linear_kernelized_attention_amd", "csrc", ent["source"])
-    if not os.path.exists(src) or sha256_of(src) != ent.get("source_sha256"):
+    if sources_sha256(ent.get("sources", [])) != ent.get("sources_sha256"):
         return None
     return float(ent["bytes_per_launch"])
 
@@ -179,14 +184,18 @@ def cpu_baseline(I, w, min_seconds=10.0):
     }
 
 
-def calibrate_copy(steps=10, mib=1024):
-    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+def calibrate_copy(steps=5, mib=1024):
+    """Plain device copies of known size (1 GiB read + 1 GiB written), for
+    scaling the FETCH_SIZE/WRITE_SIZE counters: the runtime copy kernel and
+    an elementwise kernel with 16-byte vector loads like this library's."""
     import torch
     n = mib * (1 << 20) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     for _ in range(steps):
         y.copy_(x)
+    for _ in range(steps):
+        torch.add(x, 0.5, out=y)
     torch.cuda.synchronize()
     return mib * (1 << 20)
 
