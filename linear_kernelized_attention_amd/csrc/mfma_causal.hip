@@ -40,8 +40,8 @@ __device__ inline int ct_index(int row, int s) {
 }
 
 // ------------------------------------------------------------------ scan
-// start[seg] = sum_{s < seg} part[s] over [seg][head][F][72], float32, in a
-// fixed order; one thread per 8 consecutive elements.
+// start[seg] = sum_{s < seg} part[s] elementwise over the per-segment
+// states (any layout), float32, in a fixed order; one thread per 8 elements.
 __global__ __launch_bounds__(256) void scan_kernel(const uint16_t* __restrict__ part,
                                                    float* __restrict__ start, int n_seg,
                                                    long long per_seg8) {
@@ -110,17 +110,13 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   // running state of this wave's features: S_w[f][col] as MFMA C fragments
   floatx4 acc_s[FT][5];
   {
-    const float* st = start + ((size_t)seg * BH + bh) * (size_t)F * PCOL;
+    const float* st = start + ((size_t)seg * BH + bh) * state_elems(F);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      const int row0 = (TRIG ? (ft >> 1) * M : 0) + 32 * w + 16 * (ft & 1) + 4 * g;
+      const int tile = ((TRIG ? (ft >> 1) * M : 0) + 32 * w + 16 * (ft & 1)) / 16;
 #pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        const int col = 16 * n + c;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc_s[ft][n][r] = col < SCOL ? st[(size_t)(row0 + r) * PCOL + col] : 0.f;
-      }
+      for (int n = 0; n < 5; ++n)
+        acc_s[ft][n] = *(const floatx4*)(st + ((size_t)tile * 5 + n) * TILE_ELEMS + lane * 4);
     }
   }
 
@@ -385,7 +381,7 @@ CausalPlan plan_causal(const Problem& p) {
   const int n_fpart = p.m / rows;
   // one causal block per (head, segment); about 256 of them
   cp.keys = plan_keys(p, 256LL * n_fpart, TK);
-  cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * p.F * PCOL * sizeof(float), 256);
+  cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * state_elems(p.F) * sizeof(float), 256);
   return cp;
 }
 
@@ -405,10 +401,10 @@ hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, Ph
   float* start = (float*)((char*)b.ws + cp.keys.part_bytes);
 
   phase_begin(hook, s, "mfma_kv_state");
-  launch_kv_nw<KIND>(p, b, cp.keys, s, oscale);
+  launch_kv_nw<KIND>(p, b, cp.keys, nullptr, s, oscale);
   phase_end(hook, s);
 
-  const long long per_seg8 = p.BH * (long long)p.F * PCOL / 8;
+  const long long per_seg8 = p.BH * (long long)state_elems(p.F) / 8;
   phase_begin(hook, s, "mfma_state_scan");
   hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)b.ws, start, cp.keys.n_split, per_seg8);

@@ -23,6 +23,13 @@ constexpr int TT = 32;        // tokens per key tile
 constexpr int KPAD = 8;       // bf16 padding per LDS row
 constexpr int VPAD = 8;
 constexpr int QW = 64;        // query tokens per wave in the readout
+// A key/value state (features x 80 value columns) is stored as 16 x 16 MFMA
+// C-fragment tiles: tile (ft, n) covers features 16 ft .. 16 ft + 15 and
+// columns 16 n .. 16 n + 15; lane l = 16 g + c holds rows 4 g + r, column c,
+// r = 0..3, as 4 consecutive elements.  Columns 0..63 are the values, 64 is
+// z, 65..79 are padding (finite, never read back into a result).
+constexpr int TILE_ELEMS = 64 * 4;
+__host__ __device__ inline size_t state_elems(int F) { return (size_t)(F / 16) * 5 * TILE_ELEMS; }
 constexpr float INV_2PI = 0.15915494309189535f;
 
 __device__ inline floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
@@ -59,11 +66,13 @@ __device__ inline long long xcd_logical(long long b, long long total) {
   return (b % 8) * (total / 8) + b / 8;
 }
 
-// sin/cos of 2*pi*x via the hardware units, after exact range reduction.
+// sin/cos of 2*pi*x via the hardware units (v_sin_f32/v_cos_f32, argument
+// in revolutions).  On gfx950 they reduce the argument themselves: measured
+// against float64, the error stays at 1.2e-7 for |x| up to 1e5 revolutions
+// (and is lower than after a v_fract_f32 pre-reduction), so none is done.
 __device__ inline void sincos_rev(float x, float* s, float* c) {
-  const float f = __builtin_amdgcn_fractf(x);
-  *s = __builtin_amdgcn_sinf(f);
-  *c = __builtin_amdgcn_cosf(f);
+  *s = __builtin_amdgcn_sinf(x);
+  *c = __builtin_amdgcn_cosf(x);
 }
 
 // Position of token t (0..31) of a key tile inside the permuted K dimension
@@ -111,13 +120,24 @@ __device__ inline float octet_sum(float x) {
 }
 
 // Block = (token split, feature part, head); NW waves, wave w owns the 16
-// Omega rows r0 = part * 16 NW + 16 w .. +15.  Writes a bf16 partial
-// [split][head][F][65] for its rows (trig: sin rows r, cos rows M + r).
+// Omega rows r0 = part * 16 NW + 16 w .. +15.  Writes its tiles of the bf16
+// partial state of (split, head) (trig: sin features r, cos features M + r)
+// in the C-fragment tile layout, 8 bytes per lane.
+//
+// The key tiles stream through three LDS buffers (tile i in buffer i % 3).
+// Each tile is four steps of 32 tokens, software-pipelined across steps and
+// tiles: step s issues the contraction of step s - 1 and the projection of
+// step s + 1 on the matrix cores while the VALU maps the projection of step
+// s to features, and LDS reads run one step ahead.  Tile i + 2 is staged
+// (norms, value scaling and transposition) during tile i from registers
+// loaded one tile earlier; one barrier per tile separates the writes of a
+// buffer from its last reads three tiles before.
 template <int KIND, int NW>
 __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
                                                            const float* __restrict__ Omega,
-                                                           uint16_t* __restrict__ part, int L,
+                                                           uint16_t* __restrict__ part,
+                                                           uint16_t* __restrict__ ofrag, int L,
                                                            int M, int n_fpart, int seg_len,
                                                            long long BH, float omega_scale,
                                                            float knorm_scale) {
@@ -126,7 +146,8 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
   constexpr int NT = NW * 64;
   constexpr int NTASK = TK / 2 * 8;     // (token pair, 8-column chunk) tasks
   constexpr int CH = (NTASK + NT - 1) / NT;
-  const long long nx = (long long)gridDim.x / BH;   // blocks per head
+  constexpr int NBUF = 3;
+  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
   const long long lb = xcd_logical(blockIdx.x, gridDim.x);
   const long long bh = lb / nx;
   const int split = (int)(lb % nx) / n_fpart, fpart = (int)(lb % nx) % n_fpart;
@@ -135,19 +156,28 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
   const int F = TRIG ? 2 * M : M;
   const int r0 = fpart * 16 * NW + 16 * w;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][TK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][NCOL * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][TK * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[NBUF][NCOL * VROW];
 
-  const long long seg0 = (long long)split * seg_len;
-  const long long seg1 = min((long long)L, seg0 + seg_len);
+  const int seg0 = split * seg_len;
+  const int seg1 = min(L, seg0 + seg_len);
   const size_t head = (size_t)bh * L * D;
+  const int n_tiles = (seg1 - seg0 + TK - 1) / TK;
 
-  for (int i = tid; i < 2 * (NCOL - SCOL) * VROW; i += NT) {
-    const int b = i / ((NCOL - SCOL) * VROW), e = i % ((NCOL - SCOL) * VROW);
-    Vt[b][SCOL * VROW + e] = 0;
+  // value rows 72..79 are padding: zero them once (rows 65..71 receive
+  // copies of the z column during staging)
+  for (int i = tid; i < NBUF * 8 * VROW; i += NT) {
+    const int b = i / (8 * VROW), e = i % (8 * VROW);
+    Vt[b][72 * VROW + e] = 0;
   }
   const bf16x8 om0 = omega_frag(Omega, r0, 0, lane, omega_scale);
   const bf16x8 om1 = omega_frag(Omega, r0, 1, lane, omega_scale);
+  // The first split of the first head also publishes its Omega~ fragments
+  // for the query side: fragment (row tile r0 / 16, column half kk), lane.
+  if (ofrag != nullptr && split == 0 && bh == 0) {
+    *(bf16x8*)(ofrag + ((size_t)((r0 / 16) * 2 + 0) * 64 + lane) * 8) = om0;
+    *(bf16x8*)(ofrag + ((size_t)((r0 / 16) * 2 + 1) * 64 + lane) * 8) = om1;
+  }
 
   floatx4 acc[FT][5];
 #pragma unroll
@@ -155,33 +185,30 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
 #pragma unroll
     for (int n = 0; n < 5; ++n) acc[f][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Two register sets (A, B) of raw key/value chunks give a prefetch
-  // distance of two tiles: the loads of tile i + 2 are issued before the
-  // compute of tile i, and tile i + 1 (loaded one iteration earlier) is
-  // staged after it.
+  // Raw key/value chunks of one tile: token pair (t, t + 1) x 8 columns per
+  // task.  Tokens past the segment end load the last token of the segment
+  // (always in bounds) and get weight c_t = 0 when staged.
   struct Raw {
     u32x4 k[CH][2], v[CH][2];
   };
-  Raw ra, rb;
-  auto fetch = [&](Raw& r, long long t0) {
+  Raw raw, raw1;
+  auto fetch = [&](Raw& raw, int tile) {
+    const int t0 = seg0 + tile * TK;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int task = tid + k * NT;
+      const int task = min(tid + k * NT, NTASK - 1);
       const int t = pair_token((task >> 3) & (TK / 2 - 1)), c8 = task & 7;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const long long tok = t0 + t + h;
-        if (task < NTASK && tok < seg1) {
-          r.k[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
-          r.v[k][h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
-        } else {
-          r.k[k][h] = u32x4{0u, 0u, 0u, 0u};
-          r.v[k][h] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int tok = min(t0 + t + h, seg1 - 1);
+        raw.k[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
+        raw.v[k][h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
       }
     }
   };
-  auto stage = [&](const Raw& r, int buf, long long t0) {
+  auto stage = [&](const Raw& raw, int tile) {
+    const int buf = tile % NBUF;
+    const int t0 = seg0 + tile * TK;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
@@ -190,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
       float ct[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint16_t* kv = (const uint16_t*)&r.k[k][h];
+        const uint16_t* kv = (const uint16_t*)&raw.k[k][h];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -200,91 +227,139 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
         ss = octet_sum(ss);
         ct[h] = (t0 + t + h < seg1) ? (TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f) : 0.f;
       }
-      if (task >= NTASK) continue;
-      *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = r.k[k][0];
-      *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = r.k[k][1];
-      const uint16_t* v0 = (const uint16_t*)&r.v[k][0];
-      const uint16_t* v1 = (const uint16_t*)&r.v[k][1];
+      if (CH * NT != NTASK && task >= NTASK) continue;
+      *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = raw.k[k][0];
+      *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = raw.k[k][1];
+      const uint16_t* v0 = (const uint16_t*)&raw.v[k][0];
+      const uint16_t* v1 = (const uint16_t*)&raw.v[k][1];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *(uint32_t*)&Vt[buf][vt_index(c8 * 8 + i, 2 * q)] =
             pack2(bf16_to_f32(v0[i]) * ct[0], bf16_to_f32(v1[i]) * ct[1]);
-      if (c8 == 0) *(uint32_t*)&Vt[buf][vt_index(D, 2 * q)] = pack2(ct[0], ct[1]);
-    }
-  };
-  auto compute = [&](int buf) {
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vt = Vt[buf];
-#pragma unroll
-    for (int kh = 0; kh < TK / 32; ++kh) {
-      // projection of the two 16-token sub-tiles of this k-step
-      floatx4 P[2];
-#pragma unroll
-      for (int tsub = 0; tsub < 2; ++tsub) {
-        const int row = 32 * kh + 16 * tsub + c;
-        const bf16x8 k0 = *(const bf16x8*)&ks[row * KROW + 8 * g];
-        const bf16x8 k1 = *(const bf16x8*)&ks[row * KROW + 32 + 8 * g];
-        floatx4 p = {0.f, 0.f, 0.f, 0.f};
-        p = mfma16(k0, om0, p);
-        P[tsub] = mfma16(k1, om1, p);
-      }
-      bf16x8 vf[5];
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        const int row = 16 * n + c;
-        vf[n] = *(const bf16x8*)&vt[row * VROW + (((4 * kh + g) ^ ((row >> 3) & 7)) << 3)];
-      }
-      // A fragment slot j = 4 tsub + r <-> token 32 kh + 16 tsub + 4 g + r
-      bf16x8 fa[FT];
-      if (TRIG) {
-        float sv[8], cv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sincos_rev(P[j >> 2][j & 3], &sv[j], &cv[j]);
-        fa[0] = pack8(sv);
-        fa[FT - 1] = pack8(cv);
-      } else {
-        float rv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rv[j] = fmaxf(P[j >> 2][j & 3], 0.f);
-        fa[0] = pack8(rv);
-      }
-#pragma unroll
-      for (int n = 0; n < 5; ++n)
-#pragma unroll
-        for (int f = 0; f < FT; ++f) acc[f][n] = mfma16(fa[f], vf[n], acc[f][n]);
+      // value column D holds c_t (the z column); the lanes of the other
+      // chunks write the same word into padding columns that are never read
+      // back into a stored result
+      *(uint32_t*)&Vt[buf][vt_index(D + c8, 2 * q)] = pack2(ct[0], ct[1]);
     }
   };
 
-  const int n_tiles = (int)((seg1 - seg0 + TK - 1) / TK);
-  fetch(ra, seg0);
-  if (n_tiles > 1) fetch(rb, seg0 + TK);
-  stage(ra, 0, seg0);
-  __syncthreads();
-  for (int i = 0; i < n_tiles; i += 2) {
-    // even step: compute tile i (buffer 0), stage tile i + 1 from B
-    if (i + 2 < n_tiles) fetch(ra, seg0 + (long long)(i + 2) * TK);
-    compute(0);
-    if (i + 1 < n_tiles) stage(rb, 1, seg0 + (long long)(i + 1) * TK);
-    __syncthreads();
-    if (i + 1 >= n_tiles) break;
-    // odd step: compute tile i + 1 (buffer 1), stage tile i + 2 from A
-    if (i + 3 < n_tiles) fetch(rb, seg0 + (long long)(i + 3) * TK);
-    compute(1);
-    if (i + 2 < n_tiles) stage(ra, 0, seg0 + (long long)(i + 2) * TK);
-    __syncthreads();
-  }
-
-  uint16_t* P0 = part + ((size_t)split * BH + bh) * (size_t)F * PCOL;
+  // fragments of one 32-token step kh of a tile
+  auto ld_k = [&](const uint16_t* ks, int kh, bf16x8 (&kf)[2][2]) {
 #pragma unroll
-  for (int f = 0; f < FT; ++f) {
-    const int row0 = f * M + r0 + 4 * g;
+    for (int ts = 0; ts < 2; ++ts) {
+      const int row = 32 * kh + 16 * ts + c;
+      kf[ts][0] = *(const bf16x8*)&ks[row * KROW + 8 * g];
+      kf[ts][1] = *(const bf16x8*)&ks[row * KROW + 32 + 8 * g];
+    }
+  };
+  auto ld_v = [&](const uint16_t* vt, int kh, bf16x8 (&vf)[5]) {
 #pragma unroll
     for (int n = 0; n < 5; ++n) {
-      const int col = 16 * n + c;
-      if (col < SCOL) {
+      const int row = 16 * n + c;
+      vf[n] = *(const bf16x8*)&vt[row * VROW + (((4 * kh + g) ^ ((row >> 3) & 7)) << 3)];
+    }
+  };
+  auto proj = [&](const bf16x8 (&kf)[2][2], floatx4 (&P)[2]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) P0[(size_t)(row0 + r) * PCOL + col] = bf16_bits(acc[f][n][r]);
+    for (int ts = 0; ts < 2; ++ts) {
+      floatx4 p = {0.f, 0.f, 0.f, 0.f};
+      p = mfma16(kf[ts][0], om0, p);
+      P[ts] = mfma16(kf[ts][1], om1, p);
+    }
+  };
+  // A fragment slot j = 4 ts + r <-> token 32 kh + 16 ts + 4 g + r
+  auto feat = [&](const floatx4 (&P)[2], bf16x8 (&fa)[FT]) {
+    if (TRIG) {
+      float sv[8], cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sincos_rev(P[j >> 2][j & 3], &sv[j], &cv[j]);
+      fa[0] = pack8(sv);
+      fa[FT - 1] = pack8(cv);
+    } else {
+      float rv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rv[j] = fmaxf(P[j >> 2][j & 3], 0.f);
+      fa[0] = pack8(rv);
+    }
+  };
+  auto contr = [&](const bf16x8 (&fa)[FT], const bf16x8 (&vf)[5]) {
+#pragma unroll
+    for (int n = 0; n < 5; ++n)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) acc[f][n] = mfma16(fa[f], vf[n], acc[f][n]);
+  };
+
+  // prologue: load tiles 0 and 1 together, stage them, load tile 2,
+  // project step 0
+  fetch(raw, 0);
+  if (n_tiles > 1) fetch(raw1, 1);
+  stage(raw, 0);
+  if (n_tiles > 2) fetch(raw, 2);
+  if (n_tiles > 1) stage(raw1, 1);
+  __syncthreads();
+
+  floatx4 P[2];
+  bf16x8 kn[2][2], fprev[FT], vprev[5];
+  {
+    bf16x8 k0[2][2];
+    ld_k(Ks[0], 0, k0);
+    proj(k0, P);
+    ld_k(Ks[0], 1, kn);
+  }
+  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int f = 0; f < FT; ++f) fprev[f] = zero8;
+#pragma unroll
+  for (int n = 0; n < 5; ++n) vprev[n] = zero8;
+
+  for (int i = 0; i < n_tiles; ++i) {
+    const uint16_t* ksc = Ks[i % NBUF];
+    const uint16_t* vtc = Vt[i % NBUF];
+    const uint16_t* ksn = Ks[(i + 1) % NBUF];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 vcur[5], k2[2][2], fcur[FT];
+      floatx4 Pn[2];
+      ld_v(vtc, s, vcur);
+      ld_k(s < 2 ? ksc : ksn, (s + 2) & 3, k2);
+      contr(fprev, vprev);
+      proj(kn, Pn);
+      feat(P, fcur);
+      if (s == 1 && i + 2 < n_tiles) {
+        stage(raw, i + 2);
+        if (i + 3 < n_tiles) fetch(raw, i + 3);
       }
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) P[ts] = Pn[ts];
+#pragma unroll
+      for (int f = 0; f < FT; ++f) fprev[f] = fcur[f];
+#pragma unroll
+      for (int n = 0; n < 5; ++n) vprev[n] = vcur[n];
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) {
+        kn[ts][0] = k2[ts][0];
+        kn[ts][1] = k2[ts][1];
+      }
+      // keep the steps apart: within a step the contraction, projection
+      // and feature map are independent and interleave; across steps the
+      // scheduler would pull a contraction next to the VALU producing its
+      // operand
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+  contr(fprev, vprev);
+
+  uint16_t* P0 = part + ((size_t)split * BH + bh) * state_elems(F);
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    const int ft = (f * M + r0) / 16;
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+      u32x2 o;
+      o[0] = pack2(acc[f][n][0], acc[f][n][1]);
+      o[1] = pack2(acc[f][n][2], acc[f][n][3]);
+      *(u32x2*)(P0 + ((size_t)ft * 5 + n) * TILE_ELEMS + lane * 4) = o;
     }
   }
 }
@@ -294,7 +369,8 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
 struct Plan {
   int n_split, seg_len;   // token splits of the key side
   int nw_kv, n_fpart;     // waves per kv block, feature parts per head
-  size_t part_bytes, frag_bytes, ofrag_bytes;
+  size_t part_bytes;      // bf16 partial states [n_split][BH] in tile layout
+  size_t ofrag_bytes;     // bf16 Omega~ A fragments [m / 16][2][64][8]
 };
 
 // target_blocks: kv blocks wanted over the whole grid; seg_quantum: segment
@@ -314,8 +390,7 @@ inline Plan plan_keys(const Problem& p, long long target_blocks, int seg_quantum
   seg = (seg + seg_quantum - 1) / seg_quantum * seg_quantum;
   pl.seg_len = (int)seg;
   pl.n_split = (int)((p.L + seg - 1) / seg);
-  pl.part_bytes = align_up((size_t)pl.n_split * p.BH * p.F * PCOL * sizeof(uint16_t), 256);
-  pl.frag_bytes = align_up((size_t)p.BH * (p.F / 32) * 5 * 512 * sizeof(uint16_t), 256);
+  pl.part_bytes = align_up((size_t)pl.n_split * p.BH * state_elems(p.F) * sizeof(uint16_t), 256);
   pl.ofrag_bytes = align_up((size_t)(p.m / 16) * 2 * 512 * sizeof(uint16_t), 256);
   return pl;
 }
@@ -327,24 +402,26 @@ inline dim3 head_grid(long long x, long long BH) {
 }
 
 template <int KIND, int NW>
-inline void launch_kv(const Problem& p, const Buffers& b, const Plan& pl, hipStream_t s, float oscale) {
+inline void launch_kv(const Problem& p, const Buffers& b, const Plan& pl, uint16_t* ofrag,
+                      hipStream_t s, float oscale) {
   hipLaunchKernelGGL((kv_state_kernel<KIND, NW>), dim3((unsigned)((long long)pl.n_split * pl.n_fpart * p.BH)),
                      dim3(NW * 64), 0, s, (const uint16_t*)b.k, (const uint16_t*)b.v, b.omega,
-                     (uint16_t*)b.ws, p.L, p.m, pl.n_fpart, pl.seg_len, p.BH, oscale,
+                     (uint16_t*)b.ws, ofrag, p.L, p.m, pl.n_fpart, pl.seg_len, p.BH, oscale,
                      1.0f / sqrtf((float)D));
 }
 
 template <int KIND>
-inline void launch_kv_nw(const Problem& p, const Buffers& b, const Plan& pl, hipStream_t s, float oscale) {
+inline void launch_kv_nw(const Problem& p, const Buffers& b, const Plan& pl, uint16_t* ofrag,
+                         hipStream_t s, float oscale) {
   switch (pl.nw_kv) {
-    case 1: launch_kv<KIND, 1>(p, b, pl, s, oscale); break;
-    case 2: launch_kv<KIND, 2>(p, b, pl, s, oscale); break;
-    case 3: launch_kv<KIND, 3>(p, b, pl, s, oscale); break;
-    case 4: launch_kv<KIND, 4>(p, b, pl, s, oscale); break;
-    case 5: launch_kv<KIND, 5>(p, b, pl, s, oscale); break;
-    case 6: launch_kv<KIND, 6>(p, b, pl, s, oscale); break;
-    case 7: launch_kv<KIND, 7>(p, b, pl, s, oscale); break;
-    default: launch_kv<KIND, 8>(p, b, pl, s, oscale); break;
+    case 1: launch_kv<KIND, 1>(p, b, pl, ofrag, s, oscale); break;
+    case 2: launch_kv<KIND, 2>(p, b, pl, ofrag, s, oscale); break;
+    case 3: launch_kv<KIND, 3>(p, b, pl, ofrag, s, oscale); break;
+    case 4: launch_kv<KIND, 4>(p, b, pl, ofrag, s, oscale); break;
+    case 5: launch_kv<KIND, 5>(p, b, pl, ofrag, s, oscale); break;
+    case 6: launch_kv<KIND, 6>(p, b, pl, ofrag, s, oscale); break;
+    case 7: launch_kv<KIND, 7>(p, b, pl, ofrag, s, oscale); break;
+    default: launch_kv<KIND, 8>(p, b, pl, ofrag, s, oscale); break;
   }
 }
 

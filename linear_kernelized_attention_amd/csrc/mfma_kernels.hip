@@ -21,113 +21,72 @@
 // trip: a contraction over tokens (or features) may visit its terms in any
 // order, so the other operand is stored in the matching permuted order.
 //
-// Bidirectional path, three kernels:
-//  kv_state : grid (splits, heads); wave w owns Omega rows [32w, 32w+32).
-//             Per 32-token tile: P = K~ Omega_w^T (tokens x rows) -> sin/cos
-//             -> bf16 A fragments (features x tokens) -> S_w += phi^T V' with
-//             V' = [c_t v_t | c_t | 0...] (80 columns, column 64 holds z).
-//             Writes a float32 partial [F][65] per split.
-//  reduce   : sums the split partials in a fixed order and writes S^T in
-//             the readout's A-fragment order (bf16), z replicated over the
-//             16 rows of the fifth column tile.
-//  readout  : per wave 64 query tokens: P^T = Omega~ Q~^T (rows x tokens)
-//             -> features -> out^T = S^T phi(Q)^T; the fifth row tile yields
-//             the denominator for every token; out = num / den, bf16 stores.
+// Bidirectional path, two kernels:
+//  kv_state : grid (token splits x feature parts x heads); wave w owns 16
+//             Omega rows.  Per 32 tokens: P = K~ Omega_w^T (tokens x rows)
+//             -> sin/cos -> bf16 A fragments (features x tokens) -> S_w +=
+//             phi^T V' with V' = [c_t v_t | c_t | 0...] (80 columns, column
+//             64 holds z).  Writes a bf16 partial state per split.
+//  readout  : sums the split partials in a fixed order into S^T A fragments
+//             (LDS), then per wave 64 query tokens: P^T = Omega~ Q~^T (rows x
+//             tokens) -> features -> out^T = S^T phi(Q)^T; the fifth row tile
+//             yields the denominator; out = num / den, bf16 stores.
+// With more token splits than the readout sums itself, split_sum adds them
+// up first.
 #include "mfma_common.h"
 
 namespace favor {
 namespace mfma {
 namespace {
 
-// ---------------------------------------------------------------- reduce
-// Block = (k-step, head).  k-step ks covers Omega rows 32 i .. 32 i + 31
-// (trig: i = ks / 2, s = ks % 2 picks sin/cos; relu: i = ks); slot j of
-// lane group g is row 32 i + (j < 4 ? 4 g + j : 16 + 4 g + j - 4).  Sums the
-// split partials in a fixed order (coalesced, via LDS) and writes the five
-// bf16 A fragments (column tiles; the fifth holds z in all 16 rows).
-template <int KIND>
-__global__ __launch_bounds__(256) void reduce_kernel(const uint16_t* __restrict__ part,
-                                                     uint16_t* __restrict__ sfrag,
-                                                     const float* __restrict__ Omega,
-                                                     uint16_t* __restrict__ ofrag, int M,
-                                                     int n_split, long long BH,
-                                                     float omega_scale) {
-  constexpr bool TRIG = KIND == KIND_TRIG;
-  const int F = TRIG ? 2 * M : M;
-  const int n_ks = F / 32;
-  const long long nred = (long long)n_ks * BH;
-  if ((long long)blockIdx.x >= nred) {
-    // trailing blocks: the scaled bf16 Omega~ fragments shared by every
-    // readout block (fragment i: lane i % 64, k-step (i / 64) % 2, rows
-    // 16 (i / 128) ..)
-    const long long i = ((long long)blockIdx.x - nred) * 256 + threadIdx.x;
-    if (i < (long long)(M / 16) * 2 * 64) {
-      const int l = (int)(i & 63), kk = (int)((i >> 6) & 1), ot = (int)(i >> 7);
-      *(bf16x8*)(ofrag + (size_t)i * 8) = omega_frag(Omega, 16 * ot, kk, l, omega_scale);
+// ------------------------------------------------------------ split sum
+// Elementwise float32 sum of n_split partial states (any layout, bf16) in a
+// fixed order, rounded to bf16 once: used when a head has more token splits
+// than the readout sums itself.
+__global__ __launch_bounds__(256) void split_sum_kernel(const uint16_t* __restrict__ part,
+                                                        uint16_t* __restrict__ red, int n_split,
+                                                        long long per_split8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_split8) return;
+  float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 4 <= n_split; sp += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = *(const u32x4*)(part + ((size_t)(sp + k) * per_split8 + i) * 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint16_t* h = (const uint16_t*)&v[k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] += bf16_to_f32(h[e]);
     }
-    return;
   }
-  const long long lb = xcd_logical(blockIdx.x, nred);
-  const long long bh = lb / n_ks;
-  const int ks = (int)(lb % n_ks);
-  const int i = TRIG ? ks >> 1 : ks;
-  const int s = TRIG ? ks & 1 : 0;
-  const int fbase = s * M + 32 * i;
-  __shared__ float rows[32][PCOL + 1];
-  // 32 rows x 72 columns = 288 chunks of 8 bf16 per split; all loads of a
-  // thread are issued before any is summed
-  constexpr int NCH = 32 * PCOL / 8;
-  constexpr int MAXS = 8;   // splits handled per pass
-  for (int sp0 = 0; sp0 < n_split || sp0 == 0; sp0 += MAXS) {
-    const int ns = min(MAXS, n_split - sp0);
+  for (; sp < n_split; ++sp) {
+    const u32x4 v = *(const u32x4*)(part + ((size_t)sp * per_split8 + i) * 8);
+    const uint16_t* h = (const uint16_t*)&v;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int ch = threadIdx.x + 256 * k;
-      if (ch >= NCH) continue;
-      u32x4 v[MAXS];
-#pragma unroll
-      for (int sp = 0; sp < MAXS; ++sp)
-        if (sp < ns)
-          v[sp] = *(const u32x4*)(part + (((size_t)(sp0 + sp) * BH + bh) * F + fbase) * PCOL + ch * 8);
-      float sum[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum[e] = sp0 ? rows[(ch * 8 + e) / PCOL][(ch * 8 + e) % PCOL] : 0.f;
-#pragma unroll
-      for (int sp = 0; sp < MAXS; ++sp)
-        if (sp < ns) {
-          const uint16_t* h = (const uint16_t*)&v[sp];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sum[e] += bf16_to_f32(h[e]);
-        }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rows[(ch * 8 + e) / PCOL][(ch * 8 + e) % PCOL] = sum[e];
-    }
-    if (sp0 + MAXS >= n_split) break;
+    for (int e = 0; e < 8; ++e) sum[e] += bf16_to_f32(h[e]);
   }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 5 * 64; q += 256) {
-    const int mt = q >> 6, l = q & 63, c = l & 15, g = l >> 4;
-    const int col = mt < 4 ? 16 * mt + c : D;
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = rows[j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4)][col];
-    *(bf16x8*)(sfrag + (((size_t)bh * n_ks + ks) * 5 + mt) * 512 + (size_t)l * 8) = pack8(v);
-  }
+  *(bf16x8*)(red + (size_t)i * 8) = pack8(sum);
 }
 
 // --------------------------------------------------------------- readout
 // Block = (query block, head); NW waves, QW = 64 query tokens per wave.
-// S^T (bf16 A fragments, all features) and Omega~ (A fragments) sit in LDS.
-// Per Omega row pair i (32 rows): projection P^T = Omega~ Q~^T for 4 token
-// tiles, features (B fragments, features x tokens), then the readout
-// out^T += S^T phi^T.  The loop is fully unrolled and software-pipelined:
-// the feature map of pair i is independent of the projection of pair i + 1
-// and the readout of pair i - 1, so the scheduler can overlap the VALU
-// (sin/cos) with the matrix cores.
+// The prologue loads the wave's query fragments, copies the Omega~ A
+// fragments (published by kv_state) and sums the head's nsum partial states
+// (C-fragment tiles, at part + s * split_stride) into S^T A fragments (bf16,
+// all features; the fifth column tile carries z in all 16 rows), all in LDS.  Then, per Omega row pair i (32 rows): projection
+// P^T = Omega~ Q~^T for 4 token tiles, features (B fragments, features x
+// tokens), and the readout out^T += S^T phi^T.  The loop is fully unrolled
+// and software-pipelined: the feature map of pair i is independent of the
+// projection of pair i + 1 and the readout of pair i - 1.
+constexpr int RO_MAXSUM = 4;   // partial states the readout sums itself
+
 template <int KIND, int NW, int NPAIR>
 __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ ofrag,
-                                                          const uint16_t* __restrict__ sfrag,
+                                                          const uint16_t* __restrict__ part,
+                                                          long long split_stride, int nsum,
                                                           uint16_t* __restrict__ out, int L,
                                                           long long BH) {
   constexpr bool TRIG = KIND == KIND_TRIG;
@@ -136,49 +95,108 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
   constexpr int NKS = F / 32;
   constexpr int NOT = M / 16;
   constexpr int FT = TRIG ? 2 : 1;
+  constexpr int NT = NW * 64;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const long long nx = (long long)gridDim.x / BH;   // blocks per head
+  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
   const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  const long long bh = lb / nx, qblock = lb % nx;
+  const long long bh = lb / nx;
+  const int qblock = (int)(lb % nx);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   uint16_t* Sl = smem;                    // NKS * 5 fragments
   uint16_t* Ol = smem + NKS * 5 * 512;    // NOT * 2 fragments
 
-  // Stage S^T and Omega~ fragments: every load is issued before the first
-  // LDS store so the block pays one memory latency, not one per chunk.
-  {
-    constexpr int NS = NKS * 5 * 64;                 // 16-byte chunks of S^T
-    constexpr int NO = NOT * 2 * 64;                 // 16-byte chunks of Omega~
-    constexpr int CT = (NS + NO + NW * 64 - 1) / (NW * 64);
-    const u32x4* src = (const u32x4*)(sfrag + (size_t)bh * NKS * 5 * 512);
-    const u32x4* osrc = (const u32x4*)ofrag;
-    u32x4 v[CT];
-#pragma unroll
-    for (int k = 0; k < CT; ++k) {
-      const int i = tid + k * NW * 64;
-      if (i < NS) v[k] = src[i];
-      else if (i < NS + NO) v[k] = osrc[i - NS];
-    }
-#pragma unroll
-    for (int k = 0; k < CT; ++k) {
-      const int i = tid + k * NW * 64;
-      if (i < NS + NO) ((u32x4*)smem)[i] = v[k];
-    }
-  }
-
-  const long long t0 = qblock * NW * QW + (long long)w * QW;
+  // query fragments first: their memory latency overlaps the staging
+  const long long t0 = (long long)qblock * NW * QW + (long long)w * QW;
   const size_t head = (size_t)bh * L * D;
   bf16x8 qf[4][2];
+  // tokens past L load the last token (in bounds); their outputs are not
+  // stored
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const long long tok = t0 + 16 * nt + c;
+    const long long tok = min(t0 + 16 * nt + c, (long long)L - 1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (tok < L) v = *(const u32x4*)(Q + head + (size_t)tok * D + 32 * kk + 8 * g);
-      qf[nt][kk] = __builtin_bit_cast(bf16x8, v);
+    for (int kk = 0; kk < 2; ++kk)
+      qf[nt][kk] = *(const bf16x8*)(Q + head + (size_t)tok * D + 32 * kk + 8 * g);
+  }
+
+  // S^T fragment (ks, mt), lane l = 16 g + c: slots 0..3 are the C tile of
+  // features fbase .. fbase + 15 at lane l (or lane 16 g for the z tile),
+  // slots 4..7 the tile of features fbase + 16 ..; fbase = 32 ks (relu) or
+  // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  All loads of a batch
+  // are issued before any is summed.
+  {
+    constexpr int NS = NKS * 5 * 64;
+    constexpr int NO = NOT * 2 * 64;   // 16-byte chunks of Omega~
+    constexpr int CO = (NO + NT - 1) / NT;
+    u32x4 ov[CO];
+#pragma unroll
+    for (int k = 0; k < CO; ++k) ov[k] = ((const u32x4*)ofrag)[min(tid + k * NT, NO - 1)];
+    auto item_off = [&](int item) {
+      const int ks = item / 320, mt = (item % 320) >> 6, l = item & 63;
+      const int fbase = TRIG ? (ks & 1) * M + 32 * (ks >> 1) : 32 * ks;
+      const int src = mt < 4 ? l : (l & 48);
+      return ((fbase / 16) * 5 + mt) * TILE_ELEMS + src * 4;
+    };
+    const uint16_t* pb = part + (size_t)bh * state_elems(F);
+    if (nsum == 1) {
+      constexpr int BATCH = 10;
+      for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
+        u32x2 v[BATCH][2];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          const int off = item_off(min(i0 + b * NT, NS - 1));
+          v[b][0] = *(const u32x2*)(pb + off);
+          v[b][1] = *(const u32x2*)(pb + off + 5 * TILE_ELEMS);
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b)
+          if (i0 + b * NT < NS) {
+            u32x4 o;
+            o[0] = v[b][0][0];
+            o[1] = v[b][0][1];
+            o[2] = v[b][1][0];
+            o[3] = v[b][1][1];
+            *(u32x4*)(Sl + (size_t)(i0 + b * NT) * 8) = o;
+          }
+      }
+    } else {
+      constexpr int BATCH = 5;
+      // splits past nsum re-read the last one and are not summed, so every
+      // load is unconditional
+      const uint16_t* sb[RO_MAXSUM];
+#pragma unroll
+      for (int sp = 0; sp < RO_MAXSUM; ++sp) sb[sp] = pb + (size_t)min(sp, nsum - 1) * split_stride;
+      for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
+        u32x2 v[BATCH][2][RO_MAXSUM];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          const int off = item_off(min(i0 + b * NT, NS - 1));
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int sp = 0; sp < RO_MAXSUM; ++sp)
+              v[b][h][sp] = *(const u32x2*)(sb[sp] + off + h * 5 * TILE_ELEMS);
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          const int item = i0 + b * NT;
+          float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int sp = 0; sp < RO_MAXSUM; ++sp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint16_t* e = (const uint16_t*)&v[b][h][sp];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sum[4 * h + r] += sp < nsum ? bf16_to_f32(e[r]) : 0.f;
+            }
+          if (item < NS) *(bf16x8*)(Sl + (size_t)item * 8) = pack8(sum);
+        }
+      }
     }
+#pragma unroll
+    for (int k = 0; k < CO; ++k)
+      if (tid + k * NT < NO) ((u32x4*)Ol)[tid + k * NT] = ov[k];
   }
   __syncthreads();
   if (t0 >= L) return;
@@ -284,8 +302,8 @@ size_t readout_lds(const Problem& p) {
 }
 
 template <int KIND, int NPAIR>
-void launch_readout(const Problem& p, const Buffers& b, const uint16_t* frag,
-                    const uint16_t* ofrag, hipStream_t s) {
+void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
+                    int nsum, const uint16_t* ofrag, hipStream_t s) {
   auto kern = readout_kernel<KIND, RO_NW, NPAIR>;
   // The readout stages up to 160 KB of LDS (the gfx950 maximum per block).
   static const bool attr = [&] {
@@ -295,22 +313,30 @@ void launch_readout(const Problem& p, const Buffers& b, const uint16_t* frag,
   (void)attr;
   const long long nb = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(RO_NW * 64), readout_lds(p), s,
-                     (const uint16_t*)b.q, ofrag, frag, (uint16_t*)b.out, p.L, p.BH);
+                     (const uint16_t*)b.q, ofrag, part, split_stride, nsum, (uint16_t*)b.out, p.L,
+                     p.BH);
 }
 
 template <int KIND>
-void launch_readout_m(const Problem& p, const Buffers& b, const uint16_t* frag,
-                      const uint16_t* ofrag, hipStream_t s) {
+void launch_readout_m(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
+                      int nsum, const uint16_t* ofrag, hipStream_t s) {
   switch (p.m / 32) {
-    case 1: launch_readout<KIND, 1>(p, b, frag, ofrag, s); break;
-    case 2: launch_readout<KIND, 2>(p, b, frag, ofrag, s); break;
-    case 3: launch_readout<KIND, 3>(p, b, frag, ofrag, s); break;
-    case 4: launch_readout<KIND, 4>(p, b, frag, ofrag, s); break;
-    case 5: launch_readout<KIND, 5>(p, b, frag, ofrag, s); break;
-    case 6: launch_readout<KIND, 6>(p, b, frag, ofrag, s); break;
-    case 7: launch_readout<KIND, 7>(p, b, frag, ofrag, s); break;
-    default: launch_readout<KIND, 8>(p, b, frag, ofrag, s); break;
+    case 1: launch_readout<KIND, 1>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 2: launch_readout<KIND, 2>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 3: launch_readout<KIND, 3>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 4: launch_readout<KIND, 4>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 5: launch_readout<KIND, 5>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 6: launch_readout<KIND, 6>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 7: launch_readout<KIND, 7>(p, b, part, split_stride, nsum, ofrag, s); break;
+    default: launch_readout<KIND, 8>(p, b, part, split_stride, nsum, ofrag, s); break;
   }
+}
+
+// bf16 elements of one partial state per head set, and the bytes of the
+// summed state used when the readout cannot sum the splits itself
+size_t split_stride_elems(const Problem& p) { return (size_t)p.BH * state_elems(p.F); }
+size_t red_bytes(const Problem& p, const Plan& pl) {
+  return pl.n_split > RO_MAXSUM ? align_up(split_stride_elems(p) * sizeof(uint16_t), 256) : 0;
 }
 
 template <int KIND>
@@ -318,22 +344,28 @@ hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook
   const Plan pl = plan_keys(p, 256, TK);
   const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
   uint16_t* part = (uint16_t*)b.ws;
-  uint16_t* frag = (uint16_t*)((char*)b.ws + pl.part_bytes);
-  uint16_t* ofrag = (uint16_t*)((char*)b.ws + pl.part_bytes + pl.frag_bytes);
+  uint16_t* ofrag = (uint16_t*)((char*)b.ws + pl.part_bytes + red_bytes(p, pl));
+  const long long stride = (long long)split_stride_elems(p);
 
   phase_begin(hook, s, "mfma_kv_state");
-  launch_kv_nw<KIND>(p, b, pl, s, oscale);
+  launch_kv_nw<KIND>(p, b, pl, ofrag, s, oscale);
   phase_end(hook, s);
 
-  phase_begin(hook, s, "mfma_state_reduce");
-  const long long n_oblocks = ((long long)(p.m / 16) * 2 * 64 + 255) / 256;
-  hipLaunchKernelGGL(reduce_kernel<KIND>, dim3((unsigned)((long long)(p.F / 32) * p.BH + n_oblocks)),
-                     dim3(256), 0, s, (const uint16_t*)part, frag, b.omega, ofrag, p.m, pl.n_split,
-                     p.BH, oscale);
-  phase_end(hook, s);
+  const uint16_t* src = part;
+  int nsum = pl.n_split;
+  if (pl.n_split > RO_MAXSUM) {
+    uint16_t* red = (uint16_t*)((char*)b.ws + pl.part_bytes);
+    const long long per8 = stride / 8;
+    phase_begin(hook, s, "mfma_split_sum");
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((per8 + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)part, red, pl.n_split, per8);
+    phase_end(hook, s);
+    src = red;
+    nsum = 1;
+  }
 
   phase_begin(hook, s, "mfma_readout");
-  launch_readout_m<KIND>(p, b, frag, ofrag, s);
+  launch_readout_m<KIND>(p, b, src, stride, nsum, ofrag, s);
   phase_end(hook, s);
   return hipGetLastError();
 }
@@ -353,7 +385,7 @@ bool supports(const Problem& p) {
 size_t workspace_bytes(const Problem& p) {
   if (p.causal) return causal_workspace_bytes(p);
   const Plan pl = plan_keys(p, 256, TK);
-  return pl.part_bytes + pl.frag_bytes + pl.ofrag_bytes;
+  return pl.part_bytes + red_bytes(p, pl) + pl.ofrag_bytes;
 }
 
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
