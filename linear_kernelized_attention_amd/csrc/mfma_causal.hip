@@ -115,8 +115,10 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     for (int ft = 0; ft < FT; ++ft) {
       const int tile = ((TRIG ? (ft >> 1) * M : 0) + 32 * w + 16 * (ft & 1)) / 16;
 #pragma unroll
-      for (int n = 0; n < 5; ++n)
-        acc_s[ft][n] = *(const floatx4*)(st + ((size_t)tile * 5 + n) * TILE_ELEMS + lane * 4);
+      for (int n = 0; n < 4; ++n) acc_s[ft][n] = *(const floatx4*)(st + vtile_off(tile, n) + lane * 4);
+      // column 64 (z) in lane group c = 0; the padding columns start at 0
+      const floatx4 z = *(const floatx4*)(st + z_off(F, 16 * tile + 4 * g));
+      acc_s[ft][4] = c == 0 ? z : floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
 

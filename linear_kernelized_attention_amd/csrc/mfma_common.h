@@ -23,13 +23,15 @@ constexpr int TT = 32;        // tokens per key tile
 constexpr int KPAD = 8;       // bf16 padding per LDS row
 constexpr int VPAD = 8;
 constexpr int QW = 64;        // query tokens per wave in the readout
-// A key/value state (features x 80 value columns) is stored as 16 x 16 MFMA
-// C-fragment tiles: tile (ft, n) covers features 16 ft .. 16 ft + 15 and
-// columns 16 n .. 16 n + 15; lane l = 16 g + c holds rows 4 g + r, column c,
-// r = 0..3, as 4 consecutive elements.  Columns 0..63 are the values, 64 is
-// z, 65..79 are padding (finite, never read back into a result).
+// A key/value state (F features x 64 value columns, and z) is stored as
+// F (D + 1) elements: the values as 16 x 16 MFMA C-fragment tiles, tile
+// (ft, n) covering features 16 ft .. 16 ft + 15 and columns 16 n .. + 15,
+// lane l = 16 g + c holding rows 4 g + r, column c, r = 0..3, as 4
+// consecutive elements; then z[F] in feature order.
 constexpr int TILE_ELEMS = 64 * 4;
-__host__ __device__ inline size_t state_elems(int F) { return (size_t)(F / 16) * 5 * TILE_ELEMS; }
+__host__ __device__ inline size_t state_elems(int F) { return (size_t)F * (D + 1); }
+__device__ inline int vtile_off(int ft, int n) { return (ft * 4 + n) * TILE_ELEMS; }
+__device__ inline int z_off(int F, int f) { return F * D + f; }
 constexpr float INV_2PI = 0.15915494309189535f;
 
 __device__ inline floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
@@ -119,10 +121,10 @@ __device__ inline float octet_sum(float x) {
   return x;
 }
 
-// Block = (token split, feature part, head); NW waves, wave w owns the 16
-// Omega rows r0 = part * 16 NW + 16 w .. +15.  Writes its tiles of the bf16
-// partial state of (split, head) (trig: sin features r, cos features M + r)
-// in the C-fragment tile layout, 8 bytes per lane.
+// One key task = (head bh, token split, feature part), run by one block of
+// NW waves; wave w owns the 16 Omega rows r0 = part * 16 NW + 16 w .. +15.
+// Writes its tiles of the bf16 partial state of (split, head) (trig: sin
+// features r, cos features M + r) in the state layout, 8 bytes per lane.
 //
 // The key tiles stream through three LDS buffers (tile i in buffer i % 3).
 // Each tile is four steps of 32 tokens, software-pipelined across steps and
@@ -132,32 +134,30 @@ __device__ inline float octet_sum(float x) {
 // (norms, value scaling and transposition) during tile i from registers
 // loaded one tile earlier; one barrier per tile separates the writes of a
 // buffer from its last reads three tiles before.
+constexpr int KV_NBUF = 3;
+constexpr size_t KV_LDS_BYTES = (size_t)KV_NBUF * (TK * KROW + NCOL * VROW) * sizeof(uint16_t);
+
 template <int KIND, int NW>
-__global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V,
-                                                           const float* __restrict__ Omega,
-                                                           uint16_t* __restrict__ part,
-                                                           uint16_t* __restrict__ ofrag, int L,
-                                                           int M, int n_fpart, int seg_len,
-                                                           long long BH, float omega_scale,
-                                                           float knorm_scale) {
+__device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                      const float* __restrict__ Omega, uint16_t* __restrict__ part,
+                                      uint16_t* __restrict__ ofrag, int L, int M, int n_fpart,
+                                      int seg_len, long long BH,
+                                      float omega_scale, float knorm_scale, long long bh, int task,
+                                      uint16_t* lds) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr int FT = TRIG ? 2 : 1;      // feature tiles per wave (sin, cos)
   constexpr int NT = NW * 64;
   constexpr int NTASK = TK / 2 * 8;     // (token pair, 8-column chunk) tasks
   constexpr int CH = (NTASK + NT - 1) / NT;
-  constexpr int NBUF = 3;
-  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
-  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  const long long bh = lb / nx;
-  const int split = (int)(lb % nx) / n_fpart, fpart = (int)(lb % nx) % n_fpart;
+  constexpr int NBUF = KV_NBUF;
+  const int split = task / n_fpart, fpart = task % n_fpart;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int F = TRIG ? 2 * M : M;
   const int r0 = fpart * 16 * NW + 16 * w;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][TK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[NBUF][NCOL * VROW];
+  uint16_t (*Ks)[TK * KROW] = reinterpret_cast<uint16_t (*)[TK * KROW]>(lds);
+  uint16_t (*Vt)[NCOL * VROW] = reinterpret_cast<uint16_t (*)[NCOL * VROW]>(lds + NBUF * TK * KROW);
 
   const int seg0 = split * seg_len;
   const int seg1 = min(L, seg0 + seg_len);
@@ -359,9 +359,28 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
       u32x2 o;
       o[0] = pack2(acc[f][n][0], acc[f][n][1]);
       o[1] = pack2(acc[f][n][2], acc[f][n][3]);
-      *(u32x2*)(P0 + ((size_t)ft * 5 + n) * TILE_ELEMS + lane * 4) = o;
+      if (n < 4) *(u32x2*)(P0 + vtile_off(ft, n) + lane * 4) = o;
+      else if (c == 0) *(u32x2*)(P0 + z_off(F, 16 * ft + 4 * g)) = o;   // column 64: z
     }
   }
+}
+
+// Standalone key-side kernel: one task per block, blocks numbered so that
+// the tasks of a head run on one XCD.
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __restrict__ K,
+                                                           const uint16_t* __restrict__ V,
+                                                           const float* __restrict__ Omega,
+                                                           uint16_t* __restrict__ part,
+                                                           uint16_t* __restrict__ ofrag, int L,
+                                                           int M, int n_fpart, int seg_len,
+                                                           long long BH, float omega_scale,
+                                                           float knorm_scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KV_LDS_BYTES / sizeof(uint16_t)];
+  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
+  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
+  kv_state_block<KIND, NW>(K, V, Omega, part, ofrag, L, M, n_fpart, seg_len, BH, omega_scale,
+                           knorm_scale, lb / nx, (int)(lb % nx), lds);
 }
 
 // ------------------------------------------------------- key-side host
@@ -369,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
 struct Plan {
   int n_split, seg_len;   // token splits of the key side
   int nw_kv, n_fpart;     // waves per kv block, feature parts per head
-  size_t part_bytes;      // bf16 partial states [n_split][BH] in tile layout
+  size_t part_bytes;      // bf16 partial states [n_split][BH] in the state layout
   size_t ofrag_bytes;     // bf16 Omega~ A fragments [m / 16][2][64][8]
 };
 

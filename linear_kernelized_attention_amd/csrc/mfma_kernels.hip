@@ -71,24 +71,28 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const uint16_t* __restri
 }
 
 // --------------------------------------------------------------- readout
-// Block = (query block, head); NW waves, QW = 64 query tokens per wave.
-// The prologue loads the wave's query fragments, copies the Omega~ A
-// fragments (published by kv_state) and sums the head's nsum partial states
-// (C-fragment tiles, at part + s * split_stride) into S^T A fragments (bf16,
-// all features; the fifth column tile carries z in all 16 rows), all in LDS.  Then, per Omega row pair i (32 rows): projection
+// One query task = (head bh, query block), run by one block of NW waves,
+// QW = 64 query tokens per wave.  The prologue issues the wave's query
+// fragment loads and the copy of the Omega~ A fragments (published by
+// kv_state), then sums the head's nsum partial states (at part + s *
+// split_stride) into S^T A fragments (bf16, all features; the fifth
+// fragment carries z in all 16 rows), all in LDS.  Then, per Omega row pair i (32 rows): projection
 // P^T = Omega~ Q~^T for 4 token tiles, features (B fragments, features x
 // tokens), and the readout out^T += S^T phi^T.  The loop is fully unrolled
 // and software-pipelined: the feature map of pair i is independent of the
 // projection of pair i + 1 and the readout of pair i - 1.
 constexpr int RO_MAXSUM = 4;   // partial states the readout sums itself
 
+template <int M, int F>
+constexpr size_t readout_lds_bytes() {
+  return ((size_t)(F / 32) * 5 + (size_t)(M / 16) * 2) * 512 * sizeof(uint16_t);
+}
+
 template <int KIND, int NW, int NPAIR>
-__global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __restrict__ Q,
-                                                          const uint16_t* __restrict__ ofrag,
-                                                          const uint16_t* __restrict__ part,
-                                                          long long split_stride, int nsum,
-                                                          uint16_t* __restrict__ out, int L,
-                                                          long long BH) {
+__device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ ofrag,
+                                     const uint16_t* __restrict__ part, long long split_stride,
+                                     int nsum, uint16_t* __restrict__ out, int L, long long bh,
+                                     int qblock, uint16_t* smem) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr int M = 32 * NPAIR;
   constexpr int F = TRIG ? 2 * M : M;
@@ -96,17 +100,12 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
   constexpr int NOT = M / 16;
   constexpr int FT = TRIG ? 2 : 1;
   constexpr int NT = NW * 64;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
-  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  const long long bh = lb / nx;
-  const int qblock = (int)(lb % nx);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   uint16_t* Sl = smem;                    // NKS * 5 fragments
   uint16_t* Ol = smem + NKS * 5 * 512;    // NOT * 2 fragments
 
-  // query fragments first: their memory latency overlaps the staging
+  // query fragments first: their memory latency overlaps the rest
   const long long t0 = (long long)qblock * NW * QW + (long long)w * QW;
   const size_t head = (size_t)bh * L * D;
   bf16x8 qf[4][2];
@@ -119,24 +118,33 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
     for (int kk = 0; kk < 2; ++kk)
       qf[nt][kk] = *(const bf16x8*)(Q + head + (size_t)tok * D + 32 * kk + 8 * g);
   }
+  // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
+  constexpr int NO = NOT * 2 * 64;
+  constexpr int CO = (NO + NT - 1) / NT;
+  u32x4 ov[CO];
+#pragma unroll
+  for (int k = 0; k < CO; ++k) ov[k] = ((const u32x4*)ofrag)[min(tid + k * NT, NO - 1)];
 
   // S^T fragment (ks, mt), lane l = 16 g + c: slots 0..3 are the C tile of
-  // features fbase .. fbase + 15 at lane l (or lane 16 g for the z tile),
-  // slots 4..7 the tile of features fbase + 16 ..; fbase = 32 ks (relu) or
+  // features fbase .. fbase + 15 at lane l, slots 4..7 the tile of features
+  // fbase + 16 ..; for the fifth (z) fragment every lane of group g holds
+  // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..].  fbase = 32 ks (relu) or
   // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  All loads of a batch
   // are issued before any is summed.
   {
     constexpr int NS = NKS * 5 * 64;
-    constexpr int NO = NOT * 2 * 64;   // 16-byte chunks of Omega~
-    constexpr int CO = (NO + NT - 1) / NT;
-    u32x4 ov[CO];
-#pragma unroll
-    for (int k = 0; k < CO; ++k) ov[k] = ((const u32x4*)ofrag)[min(tid + k * NT, NO - 1)];
-    auto item_off = [&](int item) {
+    // element offsets of the two 4-element pieces of item (ks, mt, lane):
+    // value tiles of features fbase.. and fbase + 16.., or for the z tile
+    // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..]
+    auto item_off = [&](int item, int& second) {
       const int ks = item / 320, mt = (item % 320) >> 6, l = item & 63;
       const int fbase = TRIG ? (ks & 1) * M + 32 * (ks >> 1) : 32 * ks;
-      const int src = mt < 4 ? l : (l & 48);
-      return ((fbase / 16) * 5 + mt) * TILE_ELEMS + src * 4;
+      if (mt < 4) {
+        second = 4 * TILE_ELEMS;
+        return vtile_off(fbase / 16, mt) + l * 4;
+      }
+      second = 16;
+      return z_off(F, fbase + 4 * (l >> 4));
     };
     const uint16_t* pb = part + (size_t)bh * state_elems(F);
     if (nsum == 1) {
@@ -145,9 +153,10 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
         u32x2 v[BATCH][2];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-          const int off = item_off(min(i0 + b * NT, NS - 1));
+          int second;
+          const int off = item_off(min(i0 + b * NT, NS - 1), second);
           v[b][0] = *(const u32x2*)(pb + off);
-          v[b][1] = *(const u32x2*)(pb + off + 5 * TILE_ELEMS);
+          v[b][1] = *(const u32x2*)(pb + off + second);
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b)
@@ -171,12 +180,13 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
         u32x2 v[BATCH][2][RO_MAXSUM];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-          const int off = item_off(min(i0 + b * NT, NS - 1));
+          int second;
+          const int off = item_off(min(i0 + b * NT, NS - 1), second);
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int sp = 0; sp < RO_MAXSUM; ++sp)
-              v[b][h][sp] = *(const u32x2*)(sb[sp] + off + h * 5 * TILE_ELEMS);
+              v[b][h][sp] = *(const u32x2*)(sb[sp] + off + h * second);
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
     }
 #pragma unroll
     for (int k = 0; k < CO; ++k)
-      if (tid + k * NT < NO) ((u32x4*)Ol)[tid + k * NT] = ov[k];
+      if (tid + k * NT < NO) *(u32x4*)(Ol + (size_t)(tid + k * NT) * 8) = ov[k];
   }
   __syncthreads();
   if (t0 >= L) return;
@@ -294,6 +304,21 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
   }
 }
 
+// Standalone query-side kernel: one task per block.
+template <int KIND, int NW, int NPAIR>
+__global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __restrict__ Q,
+                                                          const uint16_t* __restrict__ ofrag,
+                                                          const uint16_t* __restrict__ part,
+                                                          long long split_stride, int nsum,
+                                                          uint16_t* __restrict__ out, int L,
+                                                          long long BH) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
+  const long long lb = xcd_logical(blockIdx.x, gridDim.x);
+  readout_block<KIND, NW, NPAIR>(Q, ofrag, part, split_stride, nsum, out, L, lb / nx, (int)(lb % nx),
+                                 smem);
+}
+
 // ---------------------------------------------------------------- host
 constexpr int RO_NW = 8;  // waves per readout block
 
@@ -301,16 +326,21 @@ size_t readout_lds(const Problem& p) {
   return ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t);
 }
 
+// Raise a kernel's dynamic LDS limit to the gfx950 maximum (160 KB) once.
+template <typename Kern>
+void allow_full_lds(Kern kern) {
+  static const bool done = [&] {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return true;
+  }();
+  (void)done;
+}
+
 template <int KIND, int NPAIR>
 void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
                     int nsum, const uint16_t* ofrag, hipStream_t s) {
   auto kern = readout_kernel<KIND, RO_NW, NPAIR>;
-  // The readout stages up to 160 KB of LDS (the gfx950 maximum per block).
-  static const bool attr = [&] {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    return true;
-  }();
-  (void)attr;
+  allow_full_lds(kern);
   const long long nb = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(RO_NW * 64), readout_lds(p), s,
                      (const uint16_t*)b.q, ofrag, part, split_stride, nsum, (uint16_t*)b.out, p.L,
@@ -341,8 +371,8 @@ size_t red_bytes(const Problem& p, const Plan& pl) {
 
 template <int KIND>
 hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
-  const Plan pl = plan_keys(p, 256, TK);
   const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
+  const Plan pl = plan_keys(p, 256, TK);
   uint16_t* part = (uint16_t*)b.ws;
   uint16_t* ofrag = (uint16_t*)((char*)b.ws + pl.part_bytes + red_bytes(p, pl));
   const long long stride = (long long)split_stride_elems(p);
