@@ -35,6 +35,8 @@
 // up first.
 #include "mfma_common.h"
 
+#include <type_traits>
+
 namespace favor {
 namespace mfma {
 namespace {
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const uint16_t* __restri
 // and software-pipelined: the feature map of pair i is independent of the
 // projection of pair i + 1 and the readout of pair i - 1.
 constexpr int RO_MAXSUM = 4;   // partial states the readout sums itself
+constexpr int OROW = D + 8;    // padded LDS row of the staged output
 
 template <int M, int F>
 constexpr size_t readout_lds_bytes() {
@@ -170,46 +173,52 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
           }
       }
     } else {
-      constexpr int BATCH = 5;
-      // splits past nsum re-read the last one and are not summed, so every
-      // load is unconditional
-      const uint16_t* sb[RO_MAXSUM];
+      // nsum = 2..4, each a separately unrolled pass (no per-element
+      // selects): all loads of a batch, then the float32 sums in split order
+      auto pass = [&](auto ns_tag) {
+        constexpr int NSUM = decltype(ns_tag)::value;
+        constexpr int BATCH = 20 / NSUM;
+        for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
+          u32x2 v[BATCH][2][NSUM];
 #pragma unroll
-      for (int sp = 0; sp < RO_MAXSUM; ++sp) sb[sp] = pb + (size_t)min(sp, nsum - 1) * split_stride;
-      for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
-        u32x2 v[BATCH][2][RO_MAXSUM];
+          for (int b = 0; b < BATCH; ++b) {
+            int second;
+            const int off = item_off(min(i0 + b * NT, NS - 1), second);
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-          int second;
-          const int off = item_off(min(i0 + b * NT, NS - 1), second);
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+              for (int sp = 0; sp < NSUM; ++sp)
+                v[b][h][sp] = *(const u32x2*)(pb + sp * split_stride + off + h * second);
+          }
 #pragma unroll
-            for (int sp = 0; sp < RO_MAXSUM; ++sp)
-              v[b][h][sp] = *(const u32x2*)(sb[sp] + off + h * second);
+          for (int b = 0; b < BATCH; ++b) {
+            const int item = i0 + b * NT;
+            float sum[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int sp = 0; sp < NSUM; ++sp) acc += bf16_to_f32(((const uint16_t*)&v[b][h][sp])[r]);
+                sum[4 * h + r] = acc;
+              }
+            if (item < NS) *(bf16x8*)(Sl + (size_t)item * 8) = pack8(sum);
+          }
         }
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-          const int item = i0 + b * NT;
-          float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int sp = 0; sp < RO_MAXSUM; ++sp)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint16_t* e = (const uint16_t*)&v[b][h][sp];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) sum[4 * h + r] += sp < nsum ? bf16_to_f32(e[r]) : 0.f;
-            }
-          if (item < NS) *(bf16x8*)(Sl + (size_t)item * 8) = pack8(sum);
-        }
-      }
+      };
+      if (nsum == 2) pass(std::integral_constant<int, 2>{});
+      else if (nsum == 3) pass(std::integral_constant<int, 3>{});
+      else pass(std::integral_constant<int, 4>{});
     }
 #pragma unroll
     for (int k = 0; k < CO; ++k)
       if (tid + k * NT < NO) *(u32x4*)(Ol + (size_t)(tid + k * NT) * 8) = ov[k];
   }
   __syncthreads();
-  if (t0 >= L) return;
+  // waves whose tokens all lie past L skip the work but stay for the
+  // barrier before the output staging
+  const bool active = t0 < L;
 
   floatx4 acc[5][4];
 #pragma unroll
@@ -271,36 +280,53 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(Sf[f][mt], Fr[f][nt], acc[mt][nt]);
   };
 
-  floatx4 P[2][4];
-  {
-    bf16x8 Of[2][2];
-    load_omega(0, Of);
-    proj(Of, P);
-  }
+  if (active) {
+    floatx4 P[2][4];
+    {
+      bf16x8 Of[2][2];
+      load_omega(0, Of);
+      proj(Of, P);
+    }
 #pragma unroll
-  for (int i = 0; i < NPAIR; ++i) {
-    bf16x8 Sf[FT][5], Of[2][2], Fr[FT][4];
-    load_s(i, Sf);
-    if (i + 1 < NPAIR) load_omega(i + 1, Of);
-    feat(P, Fr);
-    contract(Sf, Fr);
-    if (i + 1 < NPAIR) proj(Of, P);
+    for (int i = 0; i < NPAIR; ++i) {
+      bf16x8 Sf[FT][5], Of[2][2], Fr[FT][4];
+      load_s(i, Sf);
+      if (i + 1 < NPAIR) load_omega(i + 1, Of);
+      feat(P, Fr);
+      contract(Sf, Fr);
+      if (i + 1 < NPAIR) proj(Of, P);
+    }
   }
 
-  // out^T fragment (mt, nt): lane holds columns 16 mt + 4 g + r of token
-  // t0 + 16 nt + c; the fifth tile holds the denominator in every row.
+  // Output staging: the normalised bf16 rows go through this wave's LDS
+  // region (the fragments are dead once every wave has left the loop) so
+  // that each lane stores 16 contiguous bytes and a token row is one
+  // 128-byte line.  out^T fragment (mt, nt): lane holds columns
+  // 16 mt + 4 g + r of token t0 + 16 nt + c; the fifth tile holds the
+  // denominator in every row.
+  __syncthreads();
+  if (!active) return;
+  uint16_t* ob = smem + (size_t)w * QW * OROW;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const long long tok = t0 + 16 * nt + c;
-    if (tok >= L) continue;
     const float inv = 1.0f / acc[4][nt][0];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       u32x2 o;
       o[0] = pack2(acc[mt][nt][0] * inv, acc[mt][nt][1] * inv);
       o[1] = pack2(acc[mt][nt][2] * inv, acc[mt][nt][3] * inv);
-      *(u32x2*)(out + head + (size_t)tok * D + 16 * mt + 4 * g) = o;
+      *(u32x2*)(ob + (16 * nt + c) * OROW + 16 * mt + 4 * g) = o;
     }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < QW / 8; ++k) {
+    const int row = 8 * k + (lane >> 3), c8 = lane & 7;
+    const long long tok = t0 + row;
+    if (tok < L)
+      *(u32x4*)(out + head + (size_t)tok * D + c8 * 8) = *(const u32x4*)(ob + row * OROW + c8 * 8);
   }
 }
 
@@ -323,7 +349,9 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
 constexpr int RO_NW = 8;  // waves per readout block
 
 size_t readout_lds(const Problem& p) {
-  return ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t);
+  const size_t frags = ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t);
+  const size_t staging = (size_t)RO_NW * QW * OROW * sizeof(uint16_t);
+  return frags > staging ? frags : staging;
 }
 
 // Raise a kernel's dynamic LDS limit to the gfx950 maximum (160 KB) once.
