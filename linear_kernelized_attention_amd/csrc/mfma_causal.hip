@@ -41,18 +41,18 @@ __device__ inline int ct_index(int row, int s) {
 
 // ------------------------------------------------------------------ scan
 // start[seg] = sum_{s < seg} part[s] elementwise over the per-segment
-// states (any layout), float32, in a fixed order; one thread per 8 elements.
+// states (any layout): float32 running sums in a fixed order, stored in
+// bf16 (the chunk kernel feeds the start state to bf16 MFMA operands, and
+// continues the sum in float32); one thread per 8 elements.
 __global__ __launch_bounds__(256) void scan_kernel(const uint16_t* __restrict__ part,
-                                                   float* __restrict__ start, int n_seg,
+                                                   uint16_t* __restrict__ start, int n_seg,
                                                    long long per_seg8) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= per_seg8) return;
   float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sg = 0; sg < n_seg; ++sg) {
     const u32x4 v = *(const u32x4*)(part + ((size_t)sg * per_seg8 + i) * 8);
-    float4* dst = (float4*)(start + ((size_t)sg * per_seg8 + i) * 8);
-    dst[0] = make_float4(run[0], run[1], run[2], run[3]);
-    dst[1] = make_float4(run[4], run[5], run[6], run[7]);
+    *(bf16x8*)(start + ((size_t)sg * per_seg8 + i) * 8) = pack8(run);
     const uint16_t* h = (const uint16_t*)&v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) run[e] += bf16_to_f32(h[e]);
@@ -64,7 +64,7 @@ template <int KIND, int NW>
 __global__ __launch_bounds__(NW * 64) void causal_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ Omega,
-    const float* __restrict__ start, uint16_t* __restrict__ out, int L, int seg_len, int n_seg,
+    const uint16_t* __restrict__ start, uint16_t* __restrict__ out, int L, int seg_len, int n_seg,
     long long BH, float omega_scale, float knorm_scale) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr int M = NW * 32;
@@ -110,14 +110,19 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   // running state of this wave's features: S_w[f][col] as MFMA C fragments
   floatx4 acc_s[FT][5];
   {
-    const float* st = start + ((size_t)seg * BH + bh) * state_elems(F);
+    const uint16_t* st = start + ((size_t)seg * BH + bh) * state_elems(F);
+    auto ld4 = [&](const uint16_t* p) {
+      const u32x2 v = *(const u32x2*)p;
+      return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                     __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+    };
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int tile = ((TRIG ? (ft >> 1) * M : 0) + 32 * w + 16 * (ft & 1)) / 16;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc_s[ft][n] = *(const floatx4*)(st + vtile_off(tile, n) + lane * 4);
+      for (int n = 0; n < 4; ++n) acc_s[ft][n] = ld4(st + vtile_off(tile, n) + lane * 4);
       // column 64 (z) in lane group c = 0; the padding columns start at 0
-      const floatx4 z = *(const floatx4*)(st + z_off(F, 16 * tile + 4 * g));
+      const floatx4 z = ld4(st + z_off(F, 16 * tile + 4 * g));
       acc_s[ft][4] = c == 0 ? z : floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
@@ -213,25 +218,30 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     // (b) key features: fk[ft] A fragments (feature rows x token slots,
     //     slot j = 4 ts + r <-> token 16 ts + 4 g + r); (c) the same values,
     //     transposed into this wave's LDS region as the A fragments of the
-    //     scores (token rows x features): fragment (ts, ks), lane
-    //     16 (c / 4) + 4 g + r, slot 4 ot + c % 4.
+    //     scores (token rows x features).  Within a 32-feature k-step the
+    //     features are ordered so that slot j of lane group g is row
+    //     4 g + j / 2 of row tile j % 2: this lane's two row tiles (ot) of
+    //     a token land in adjacent slots of fragment (ts, ks), lane
+    //     16 (c / 4) + 4 g + r, slots 2 (c % 4) + ot -- one 32-bit write.
     bf16x8 fk[FT];
+    {
+      float sv[2][8], cv[2][8];
 #pragma unroll
-    for (int ot = 0; ot < 2; ++ot) {
-      float sv[8], cv[8];
+      for (int ot = 0; ot < 2; ++ot) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (TRIG) sincos_rev(PK[j >> 2][ot][j & 3], &sv[j], &cv[j]);
-        else sv[j] = fmaxf(PK[j >> 2][ot][j & 3], 0.f);
+        for (int j = 0; j < 8; ++j) {
+          if (TRIG) sincos_rev(PK[j >> 2][ot][j & 3], &sv[ot][j], &cv[ot][j]);
+          else sv[ot][j] = fmaxf(PK[j >> 2][ot][j & 3], 0.f);
+        }
+        fk[ot] = pack8(sv[ot]);
+        if (TRIG) fk[2 + ot] = pack8(cv[ot]);
       }
-      fk[ot] = pack8(sv);
-      if (TRIG) fk[2 + ot] = pack8(cv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ts = j >> 2, r = j & 3;
-        const int dl = 16 * (c >> 2) + 4 * g + r, ds = 4 * ot + (c & 3);
-        kt[((ts * KS + 0) * 64 + dl) * 8 + ds] = bf16_bits(sv[j]);
-        if (TRIG) kt[((ts * KS + 1) * 64 + dl) * 8 + ds] = bf16_bits(cv[j]);
+        const int dl = 16 * (c >> 2) + 4 * g + r, ds = 2 * (c & 3);
+        *(uint32_t*)&kt[((ts * KS + 0) * 64 + dl) * 8 + ds] = pack2(sv[0][j], sv[1][j]);
+        if (TRIG) *(uint32_t*)&kt[((ts * KS + 1) * 64 + dl) * 8 + ds] = pack2(cv[0][j], cv[1][j]);
       }
     }
     // (d) query projection P_Q^T[ot][nt]: Omega row 16 ot + 4 g + r, token 16 nt + c
@@ -248,15 +258,15 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       }
     }
     // (e) query features: B fragments (features x tokens), slot j <-> row
-    //     16 (j / 4) + 4 g + j % 4 of this wave's 32 rows
+    //     16 (j % 2) + 4 g + j / 2 of this wave's 32 rows (the order of (c))
     bf16x8 bq[KS][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float sv[8], cv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (TRIG) sincos_rev(PQ[j >> 2][nt][j & 3], &sv[j], &cv[j]);
-        else sv[j] = fmaxf(PQ[j >> 2][nt][j & 3], 0.f);
+        if (TRIG) sincos_rev(PQ[j & 1][nt][j >> 1], &sv[j], &cv[j]);
+        else sv[j] = fmaxf(PQ[j & 1][nt][j >> 1], 0.f);
       }
       bq[0][nt] = pack8(sv);
       if (TRIG) bq[KS - 1][nt] = pack8(cv);
@@ -303,21 +313,27 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    // S_prev,w^T A fragments (bf16, the feature order of (c) and (e)), once
+    // per chunk for both query halves
+    bf16x8 sa[KS][5];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 5; ++mt) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = acc_s[(KS == 2 ? 2 * s : 0) + (j & 1)][mt][j >> 1];
+        sa[s][mt] = pack8(v);
+      }
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
       floatx4 ao[5];
 #pragma unroll
       for (int mt = 0; mt < 5; ++mt) ao[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int mt = 0; mt < 5; ++mt) {
-          float v[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = acc_s[KS == 2 ? 2 * s + (j >> 2) : (j >> 2)][mt][j & 3];
-          ao[mt] = mfma16(pack8(v), bq[s][nq], ao[mt]);
-        }
-      }
+        for (int mt = 0; mt < 5; ++mt) ao[mt] = mfma16(sa[s][mt], bq[s][nq], ao[mt]);
 #pragma unroll
       for (int mt = 0; mt < 5; ++mt) {
         ao[mt] = mfma16(vf[mt], bs[nq], ao[mt]);
@@ -383,12 +399,12 @@ CausalPlan plan_causal(const Problem& p) {
   const int n_fpart = p.m / rows;
   // one causal block per (head, segment); about 256 of them
   cp.keys = plan_keys(p, 256LL * n_fpart, TK);
-  cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * state_elems(p.F) * sizeof(float), 256);
+  cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * state_elems(p.F) * sizeof(uint16_t), 256);
   return cp;
 }
 
 template <int KIND, int NW>
-void launch_causal(const Problem& p, const Buffers& b, const CausalPlan& cp, const float* start,
+void launch_causal(const Problem& p, const Buffers& b, const CausalPlan& cp, const uint16_t* start,
                    hipStream_t s, float oscale) {
   hipLaunchKernelGGL((causal_kernel<KIND, NW>), dim3((unsigned)((long long)cp.keys.n_split * p.BH)),
                      dim3(NW * 64), 0, s, (const uint16_t*)b.q, (const uint16_t*)b.k,
@@ -400,7 +416,7 @@ template <int KIND>
 hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
   const CausalPlan cp = plan_causal(p);
   const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
-  float* start = (float*)((char*)b.ws + cp.keys.part_bytes);
+  uint16_t* start = (uint16_t*)((char*)b.ws + cp.keys.part_bytes);
 
   phase_begin(hook, s, "mfma_kv_state");
   launch_kv_nw<KIND>(p, b, cp.keys, nullptr, s, oscale);
