@@ -154,6 +154,41 @@ def bench_block(F, I, steps, warmup):
     return time_calls(fn, steps, warmup)
 
 
+def bench_random(F, shape, kind, causal, steps, warmup):
+    """Seconds per favor_attention call on random bf16 inputs of a shape
+    (timing only: values N(0,1) d^-1/4 drawn on the device, Omega from the
+    seeded orthogonal draw)."""
+    import torch
+    from linear_kernelized_attention_amd import inputs as I
+    B, H, L, d, m = shape
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q, k, v = [(torch.randn(B, H, L, d, device="cuda", generator=g) * d ** -0.25).to(torch.bfloat16)
+               for _ in range(3)]
+    dr = I.omega_draws(m, d, seed=0)
+    omega = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, m)).cuda()
+    out = torch.empty_like(q)
+    need = F.favor_attention_workspace_bytes(B, H, L, d, m, "bf16", kind, causal, "auto")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    fn = lambda: F.favor_attention(q, k, v, omega, kind=kind, causal=causal, out=out, workspace=ws)
+    return time_calls(fn, steps, warmup)
+
+
+def cpu_oracle_once(I, w):
+    """tokens x heads per second of one pass of the float64 oracle on a
+    workload (one worker per head, BLAS at 1 thread)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import favor_oracle as O
+    ai, dr = I.workload_inputs(w)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, w.m)
+    workers = max(1, min(O.default_workers(), w.B * w.H))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        O.favor_attention(ai.q64, ai.k64, ai.v64, W, w.kind, w.causal, workers=workers)
+        el = time.perf_counter() - t0
+    return w.tokens_x_heads / el
+
+
 def cpu_baseline(I, w, min_seconds=10.0):
     """The float64 oracle, as it stands, on the whole headline workload
     (repeated until min_seconds of wall time), one worker thread per core."""
@@ -285,11 +320,26 @@ def main():
                           "hbm_frac": by / s / 1e9 / PEAK_HBM_GBS,
                           "phases_ms": {n: t for n, t in ph}}
         sb = bench_block(F, I, steps, 3)
-        extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": 2 * 4096 / sb}
+        cfg = I.BLOCK_WORKLOAD
+        sf = bench_random(F, (cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["m"]), cfg["kind"], False,
+                          steps, 3)
+        extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": cfg["B"] * cfg["L"] / sb,
+                             "favor_us_per_call": sf * 1e6}
+        # saturation: the headline shape at larger batch (timing on random inputs)
+        sweep = {}
+        for Bs in (8, 16, 32):
+            ss = bench_random(F, (Bs, w.H, w.L, w.d, w.m), w.kind, w.causal, steps, 3)
+            fl, _ = path_total_work(Bs, w.H, w.L, w.d, w.m, w.kind)
+            sweep[f"B{Bs}"] = {"us_per_call": ss * 1e6, "tokens_x_heads_per_s": Bs * w.H * w.L / ss,
+                               "mfma_frac": fl / ss / 1e12 / PEAK_BF16_MFMA_TFLOPS}
+        extra["head_sweep"] = sweep
         rec["extra"] = extra
 
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(I, w)
+        if "extra" in rec:
+            for key in ("c1", "c2_trig", "c2_relu", "c3_causal", "c4_bidir", "c4_causal"):
+                rec["extra"][key]["cpu_oracle_tokens_x_heads_per_s"] = cpu_oracle_once(I, I.WORKLOADS[key])
     else:
         rec["cpu_baseline"] = None
 

@@ -19,6 +19,9 @@
  *    concurrent calls on different streams are safe.
  *  - Tensors are dense row-major.  Attention tensors are [B, H, L, d] with
  *    d fastest; Omega is [m, d] float32 and shared by every (b, h).
+ *  - Device pointers (tensors and workspace) must be 16-byte aligned (the
+ *    kernels move data in 16-byte vectors); a misaligned pointer returns
+ *    FAVOR_ERR_INVALID_ARG.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
  *    work is enqueued on it asynchronously; no entry point synchronises.
  *  - Every argument check runs on the host before anything is enqueued and
@@ -150,6 +153,7 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
  * favor_embed_bf16: x[t, :] = table[ids[t], :] for t < n_tok.
  *   ids int32 [n_tok] device; table bf16 [vocab, E] device; x bf16
  *   [n_tok, E] device.  An id outside [0, vocab) writes a zero row.
+ *   Requires E a multiple of 8 (FAVOR_ERR_UNSUPPORTED otherwise).
  */
 int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int vocab, int E,
                      void* stream);

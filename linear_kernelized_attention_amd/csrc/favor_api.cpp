@@ -74,6 +74,8 @@ struct Checked {
   bool empty;
 };
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 int check_call(const void* Q, const void* K, const void* V, const float* Omega, void* out, int B,
                int H, int L, int d, int m, int dtype, int kind, int causal, void* ws,
                size_t ws_bytes_given, int path, Checked* c) {
@@ -85,6 +87,9 @@ int check_call(const void* Q, const void* K, const void* V, const float* Omega, 
     return FAVOR_OK;
   }
   if (!Q || !K || !V || !Omega || !out) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Omega) || !aligned16(out) ||
+      (ws && !aligned16(ws)))
+    return FAVOR_ERR_INVALID_ARG;
   const int r = resolve(c->p, path);
   if (r < 0) return r;
   c->path = r;
@@ -255,8 +260,10 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
 int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int vocab, int E,
                      void* stream) {
   if (n_tok < 0 || vocab < 1 || E < 1) return FAVOR_ERR_INVALID_ARG;
+  if (E % 8) return FAVOR_ERR_UNSUPPORTED;
   if (n_tok == 0) return FAVOR_OK;
   if (!ids || !table || !x) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(table) || !aligned16(x)) return FAVOR_ERR_INVALID_ARG;
   if (overlaps(x, (size_t)n_tok * E * 2, table, (size_t)vocab * E * 2) ||
       overlaps(x, (size_t)n_tok * E * 2, ids, (size_t)n_tok * 4))
     return FAVOR_ERR_ALIAS;
@@ -269,6 +276,7 @@ int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K
                       int out_heads, int seq_len, void* stream) {
   if (M < 1 || N < 1 || K < 1 || in_heads < 0 || out_heads < 0) return FAVOR_ERR_INVALID_ARG;
   if (!X || !W || !Y) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return FAVOR_ERR_INVALID_ARG;
   if (N % 32 || K % 32) return FAVOR_ERR_UNSUPPORTED;
   if (in_heads > 0 || out_heads > 0) {
     if (seq_len < 1 || M % seq_len) return FAVOR_ERR_INVALID_ARG;

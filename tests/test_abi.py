@@ -67,6 +67,16 @@ def test_invalid_arguments():
     assert call(path=9) == B.FAVOR_ERR_INVALID_ARG
 
 
+def test_misaligned_pointers():
+    # every device pointer must be 16-byte aligned
+    assert call(q=QA + 2) == B.FAVOR_ERR_INVALID_ARG
+    assert call(k=KA + 8) == B.FAVOR_ERR_INVALID_ARG
+    assert call(v=VA + 4) == B.FAVOR_ERR_INVALID_ARG
+    assert call(w=WA + 4) == B.FAVOR_ERR_INVALID_ARG
+    assert call(o=OA + 2) == B.FAVOR_ERR_INVALID_ARG
+    assert call(ws=WS + 8) == B.FAVOR_ERR_INVALID_ARG
+
+
 def test_empty_problem_is_noop():
     for kw in (dict(L=0), dict(B_=0), dict(H=0)):
         assert call(q=0, k=0, v=0, w=0, o=0, ws=0, wsb=0, **kw) == B.FAVOR_OK
@@ -115,6 +125,9 @@ def test_linear_and_embed_argument_checks():
     assert lib.favor_linear_bf16(QA, KA, OA, 100, 64, 64, 0, 2, 64, None) == B.FAVOR_ERR_INVALID_ARG
     assert lib.favor_embed_bf16(0, KA, OA, 10, 26, 512, None) == B.FAVOR_ERR_INVALID_ARG
     assert lib.favor_embed_bf16(0, 0, 0, 0, 26, 512, None) == B.FAVOR_OK
+    assert lib.favor_embed_bf16(QA, KA, OA, 10, 26, 12, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_embed_bf16(QA, KA + 2, OA, 10, 26, 512, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_linear_bf16(QA + 2, KA, OA, 64, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("m,d", [(64, 16), (256, 64), (40, 16)])
