@@ -33,7 +33,13 @@ definitions state):
      x~ = d**-0.25 * x,  P = x~ Omega^T  (L x m)
      trig: phi(x) = exp(|x~|^2 / 2) * m**-0.5 * [sin P, cos P]   (F = 2m)
      relu: phi(x) = m**-0.5 * max(P, 0)                          (F = m)
-   so that E[phi(q).phi(k)] = exp(q.k / sqrt(d)) for the trig map.
+     positive: phi(x) = m**-0.5 * exp(P - |x~|^2 / 2)            (F = m)
+   so that E[phi(q).phi(k)] = exp(q.k / sqrt(d)) for the trig and the
+   positive maps.  The positive (non-negative) map is the FAVOR+ variant
+   the blog section names but prints garbled; its form here follows from
+   the Gaussian moment-generating function E_w[exp(w.a)] = exp(|a|^2 / 2)
+   for w ~ N(0, I): E[exp(w.q~ - |q~|^2/2) exp(w.k~ - |k~|^2/2)] =
+   exp(|q~ + k~|^2 / 2 - |q~|^2 / 2 - |k~|^2 / 2) = exp(q~.k~).
 3. Bidirectional [blog §核心机制：FAVOR+]: S = phi(K)^T V, z = phi(K)^T 1,
    out_i = phi(q_i)^T S / phi(q_i)^T z.  No L x L matrix.
 4. Causal [blog §核心机制：FAVOR+, causal variant]: the same with the
@@ -58,7 +64,7 @@ from typing import Iterable, Optional, Sequence
 
 import numpy as np
 
-KINDS = ("trig", "relu")
+KINDS = ("trig", "relu", "positive")
 
 
 # --------------------------------------------------------------- step 1
@@ -102,6 +108,9 @@ def feature_map(X: np.ndarray, Omega: np.ndarray, kind: str) -> np.ndarray:
         return np.exp(half_sq_norm) * m ** -0.5 * np.concatenate([np.sin(P), np.cos(P)], axis=-1)
     if kind == "relu":
         return m ** -0.5 * np.maximum(P, 0.0)
+    if kind == "positive":
+        half_sq_norm = 0.5 * np.sum(Xt * Xt, axis=-1, keepdims=True)
+        return m ** -0.5 * np.exp(P - half_sq_norm)
     raise ValueError(f"unknown feature kind {kind!r}")
 
 

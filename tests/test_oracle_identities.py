@@ -7,7 +7,8 @@
   lower-triangular (diagonal included) masked form.
 * Special cases with closed forms: a single token, constant values,
   linearity, permutation symmetry, equal keys, the zero feature matrix
-  (which reduces the trig map to a key-norm-weighted mean), ReLU convexity.
+  (which reduces the trig map to a key-norm-weighted mean), convexity of
+  the ReLU and positive maps' outputs.
 """
 import numpy as np
 import pytest
@@ -143,13 +144,18 @@ def test_zero_features_key_norm_weighting(causal):
     assert np.allclose(out, np.broadcast_to(num / den, out.shape), rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("kind", ["relu", "positive"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_relu_rows_convex_combinations(causal):
+def test_nonnegative_maps_give_convex_combinations(kind, causal):
+    # both maps give non-negative features (positive: strictly), so every
+    # output row is a convex combination of the visible value rows
     Q, K, V, W = _case(L=60, seed=5)
-    out = O.favor_attention(Q, K, V, W, "relu", causal)
-    phq = O.feature_map(Q, W, "relu")
-    phk = O.feature_map(K, W, "relu")
+    out = O.favor_attention(Q, K, V, W, kind, causal)
+    phq = O.feature_map(Q, W, kind)
+    phk = O.feature_map(K, W, kind)
     assert np.all(phq @ np.swapaxes(phk, -1, -2) >= 0)
+    if kind == "positive":
+        assert np.all(phq > 0) and np.all(phk > 0)
     for i in range(60):
         hi = (V[..., : i + 1, :] if causal else V).max(axis=-2)
         lo = (V[..., : i + 1, :] if causal else V).min(axis=-2)
@@ -160,6 +166,7 @@ def test_feature_widths():
     Q, K, V, W = _case(m=16)
     assert O.feature_map(Q, W, "trig").shape[-1] == 32
     assert O.feature_map(Q, W, "relu").shape[-1] == 16
+    assert O.feature_map(Q, W, "positive").shape[-1] == 16
 
 
 def test_relu_scale_invariance():

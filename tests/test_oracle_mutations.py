@@ -28,6 +28,16 @@ def unbiased_trig_ok(n=3000, d=8):
     return abs(est.mean() - target) <= 4 * est.std(ddof=1) / np.sqrt(n)
 
 
+def unbiased_positive_ok(n=3000, d=8):
+    r = np.random.default_rng(1002)
+    q = r.standard_normal(d) * d ** -0.25
+    k = r.standard_normal(d) * d ** -0.25
+    target = np.exp(q @ k / np.sqrt(d))
+    est = np.array([O.feature_map(q[None], W, "positive")[0] @ O.feature_map(k[None], W, "positive")[0]
+                    for W in (_omega(8, d, s) for s in range(n))])
+    return abs(est.mean() - target) <= 4 * est.std(ddof=1) / np.sqrt(n)
+
+
 def arccos_relu_ok(n=3000, d=8):
     r = np.random.default_rng(1001)
     q = r.standard_normal(d) * d ** -0.25
@@ -75,8 +85,8 @@ def orthogonal_ok():
     return np.abs(blk @ blk.T - np.eye(8)).max() <= 1e-12
 
 
-ALL_PINS = [unbiased_trig_ok, arccos_relu_ok, zero_features_ok, causal_masked_ok,
-            constant_values_ok, orthogonal_ok]
+ALL_PINS = [unbiased_trig_ok, unbiased_positive_ok, arccos_relu_ok, zero_features_ok,
+            causal_masked_ok, constant_values_ok, orthogonal_ok]
 
 
 def test_real_oracle_passes_every_pin():
@@ -114,6 +124,23 @@ def _fm_relu_abs(X, Omega, kind):
     return Omega.shape[0] ** -0.5 * np.abs(P)
 
 
+def _fm_positive_plus_half_norm(X, Omega, kind):
+    if kind != "positive":
+        return _real_feature_map(X, Omega, kind)
+    X = np.asarray(X, float)
+    Xt = X * X.shape[-1] ** -0.25
+    P = Xt @ np.asarray(Omega, float).T
+    return Omega.shape[0] ** -0.5 * np.exp(P + 0.5 * np.sum(Xt * Xt, -1, keepdims=True))
+
+
+def _fm_positive_no_half_norm(X, Omega, kind):
+    if kind != "positive":
+        return _real_feature_map(X, Omega, kind)
+    X = np.asarray(X, float)
+    P = (X * X.shape[-1] ** -0.25) @ np.asarray(Omega, float).T
+    return Omega.shape[0] ** -0.5 * np.exp(P)
+
+
 def _orf_unit_rows(gaussian, radii, m):
     return _real_orf(gaussian, np.ones_like(radii), m)
 
@@ -148,6 +175,8 @@ MUTANTS = {
     "d^-1/2 instead of d^-1/4": ("feature_map", _fm_wrong_scale),
     "sin block used twice": ("feature_map", _fm_sin_twice),
     "relu replaced by abs": ("feature_map", _fm_relu_abs),
+    "positive with +|x|^2/2": ("feature_map", _fm_positive_plus_half_norm),
+    "positive without -|x|^2/2": ("feature_map", _fm_positive_no_half_norm),
     "ORF rows of unit norm": ("orthogonal_random_features", _orf_unit_rows),
     "ORF without Gram-Schmidt": ("orthogonal_random_features", _orf_no_orthogonalisation),
     "exclusive causal prefix": ("_causal_head", _causal_exclusive),

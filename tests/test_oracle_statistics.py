@@ -5,6 +5,8 @@
   E[phi(q).phi(k)] = exp(q.k / sqrt(d)) for the trig map, because for
   w ~ N(0, I) E[cos(w.u)] = exp(-|u|^2/2) (the Gaussian characteristic
   function) and each ORF row is marginally N(0, I).
+* Positive map: E[phi(q).phi(k)] = exp(q.k / sqrt(d)) as well, from the
+  Gaussian moment-generating function E[exp(w.a)] = exp(|a|^2/2).
 * ReLU map: E[phi(q).phi(k)] is the degree-1 arc-cosine kernel
   |x||y| (sin t + (pi - t) cos t) / (2 pi) of x~ = d^-1/4 q, y~ = d^-1/4 k
   (Cho and Saul, 2009) -- a closed form, not on the pages.
@@ -46,6 +48,17 @@ def test_trig_unbiased(pair_seed, scale):
     q, k = _pair(d, pair_seed, scale)
     target = np.exp(q @ k / np.sqrt(d))
     est = _estimates(q, k, 8, d, "trig", 6000)
+    se = est.std(ddof=1) / np.sqrt(est.size)
+    assert abs(est.mean() - target) <= 4 * se, (est.mean(), target, se)
+
+
+@pytest.mark.parametrize("pair_seed,scale", [(0, 1.0), (1, 1.0), (2, 1.4), (3, 0.5)])
+def test_positive_unbiased(pair_seed, scale):
+    d = 8
+    q, k = _pair(d, pair_seed, scale)
+    target = np.exp(q @ k / np.sqrt(d))
+    est = _estimates(q, k, 8, d, "positive", 6000)
+    assert np.all(est > 0)
     se = est.std(ddof=1) / np.sqrt(est.size)
     assert abs(est.mean() - target) <= 4 * se, (est.mean(), target, se)
 
