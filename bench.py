@@ -311,7 +311,7 @@ def main():
     if not args.no_extra:
         extra = {}
         steps = max(10, args.steps // 4)
-        for key in ("c3_causal", "c2_trig", "c2_relu", "c4_bidir", "c4_causal", "c1"):
+        for key in ("c3_causal", "c2_trig", "c2_relu", "c4_bidir", "c4_causal", "c1", "pos_bidir", "pos_causal"):
             wk = I.WORKLOADS[key]
             s, ph, rp = bench_attention(F, I, wk, steps, max(3, args.warmup // 4), "auto")
             fl, by = path_total_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind, 4 if wk.dtype == "f32" else 2)
@@ -338,7 +338,7 @@ def main():
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(I, w)
         if "extra" in rec:
-            for key in ("c1", "c2_trig", "c2_relu", "c3_causal", "c4_bidir", "c4_causal"):
+            for key in ("c1", "c2_trig", "c2_relu", "c3_causal", "c4_bidir", "c4_causal", "pos_bidir", "pos_causal"):
                 rec["extra"][key]["cpu_oracle_tokens_x_heads_per_s"] = cpu_oracle_once(I, I.WORKLOADS[key])
     else:
         rec["cpu_baseline"] = None

@@ -59,12 +59,22 @@ typedef enum { FAVOR_DTYPE_F32 = 0, FAVOR_DTYPE_BF16 = 1 } favor_dtype;
  * RELU: phi(x) = m^-1/2 max(Omega x~, 0), F = m features: generalized
  *       attention with ReLU as the kernel function (Chinese summary page,
  *       section 核心创新 item 2; English page, Technical Contribution).
- * In both, x~ = d^-1/4 x is applied by the library to the Q and K passed in. */
-typedef enum { FAVOR_FEATURE_TRIG = 0, FAVOR_FEATURE_RELU = 1 } favor_feature_kind;
+ * POSITIVE: phi(x) = m^-1/2 exp(Omega x~ - |x~|^2/2), F = m non-negative
+ *       features, also an unbiased estimate of exp(q.k/sqrt(d)) (the
+ *       positive FAVOR+ variant named in the blog section; its form follows
+ *       from the Gaussian moment-generating function).  The exponent is
+ *       evaluated as one float32 value per feature: it never exceeds
+ *       |omega|^2/2, and underflows only for |x~| far beyond the rows' norm.
+ * In all, x~ = d^-1/4 x is applied by the library to the Q and K passed in. */
+typedef enum {
+  FAVOR_FEATURE_TRIG = 0,
+  FAVOR_FEATURE_RELU = 1,
+  FAVOR_FEATURE_POSITIVE = 2
+} favor_feature_kind;
 
 /* Kernel family selection for favor_attention_ex (AUTO = the fastest path
  * that supports the request).  MFMA requires bf16, d = 64 and m a multiple
- * of 32 with m <= 512; GENERIC handles f32 and bf16 with d <= 64. */
+ * of 32 with m <= 256; GENERIC handles f32 and bf16 with d <= 64. */
 typedef enum { FAVOR_PATH_AUTO = 0, FAVOR_PATH_GENERIC = 1, FAVOR_PATH_MFMA = 2 } favor_path;
 
 /* Library version, (major << 16) | (minor << 8) | patch. */

@@ -24,7 +24,7 @@ FAVOR_ERR_ALIAS = -4
 FAVOR_ERR_HIP = -5
 
 DTYPE = {"f32": 0, "bf16": 1}
-KIND = {"trig": 0, "relu": 1}
+KIND = {"trig": 0, "relu": 1, "positive": 2}
 PATH = {"auto": 0, "generic": 1, "mfma": 2}
 PATH_NAME = {v: k for k, v in PATH.items()}
 

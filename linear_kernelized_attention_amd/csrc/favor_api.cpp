@@ -21,7 +21,8 @@ constexpr int kMaxM = 1024;
 
 bool valid_enums(int dtype, int kind, int causal) {
   return (dtype == FAVOR_DTYPE_F32 || dtype == FAVOR_DTYPE_BF16) &&
-         (kind == FAVOR_FEATURE_TRIG || kind == FAVOR_FEATURE_RELU) && (causal == 0 || causal == 1);
+         (kind == FAVOR_FEATURE_TRIG || kind == FAVOR_FEATURE_RELU || kind == FAVOR_FEATURE_POSITIVE) &&
+         (causal == 0 || causal == 1);
 }
 
 // Shape/enum checks shared by sizing and launching.  Returns FAVOR_OK,

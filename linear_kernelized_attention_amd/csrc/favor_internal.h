@@ -8,7 +8,7 @@
 
 namespace favor {
 
-enum { KIND_TRIG = 0, KIND_RELU = 1 };
+enum { KIND_TRIG = 0, KIND_RELU = 1, KIND_POS = 2 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { PATH_AUTO = 0, PATH_GENERIC = 1, PATH_MFMA = 2 };
 

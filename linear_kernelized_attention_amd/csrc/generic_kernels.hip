@@ -1,5 +1,5 @@
 // Generic FAVOR kernels: float32 arithmetic on the vector ALUs, any
-// d <= 64, any m, any L, float32 or bf16 storage, both feature maps, both
+// d <= 64, any m, any L, float32 or bf16 storage, all three feature maps, both
 // directions.  This family carries the float32 inputs and every shape the
 // MFMA family does not take.
 //
@@ -7,6 +7,7 @@
 // P = x~ Omega^T,
 //   trig: phi(x) = exp(|x~|^2/2) m^-1/2 [sin P, cos P]    (F = 2m)
 //   relu: phi(x) = m^-1/2 max(P, 0)                       (F = m)
+//   positive: phi(x) = m^-1/2 exp(P - |x~|^2/2)           (F = m)
 // bidirectional: out_i = phi(q_i)^T S / phi(q_i)^T z with S = phi(K)^T V,
 // z = phi(K)^T 1; causal: the same with inclusive prefix sums over j <= i.
 //
@@ -76,9 +77,11 @@ __device__ inline int feat_index(int fl, int r0, int rc, int m, bool trig) {
 }
 
 // phi for tile rows [0, TILE) of xs (already scaled by d^-1/4) into ph.
+// xscale[t] is the row's factor (trig, relu) or exponent offset (positive).
 __device__ inline void feature_chunk(const float (*xs)[DP], const float* xscale,
                                      const float (*om)[DP], float (*ph)[FCW], int d, int rc,
-                                     bool trig, int tid) {
+                                     int kind, int tid) {
+  const bool trig = kind == KIND_TRIG;
   const int nf = trig ? 2 * rc : rc;
   for (int i = tid; i < TILE * nf; i += NT) {
     const int t = i / nf, fl = i % nf;
@@ -90,6 +93,8 @@ __device__ inline void feature_chunk(const float (*xs)[DP], const float* xscale,
       float s, co;
       sincosf(P, &s, &co);
       val = (fl < rc ? s : co) * xscale[t];
+    } else if (kind == KIND_POS) {
+      val = expf(P - xscale[t]);
     } else {
       val = fmaxf(P, 0.f) * xscale[t];
     }
@@ -97,10 +102,12 @@ __device__ inline void feature_chunk(const float (*xs)[DP], const float* xscale,
   }
 }
 
-// Stage a tile of x (scaled by d^-1/4) and its per-row feature scale.
+// Stage a tile of x (scaled by d^-1/4) and its per-row feature scale:
+// trig exp(|x~|^2/2) m^-1/2, relu m^-1/2; positive the exponent offset
+// |x~|^2/2 - ln(m^-1/2), so that phi = exp(P - offset) = m^-1/2 exp(P - |x~|^2/2).
 template <typename T>
 __device__ inline void load_scaled(const T* X, long long t0, long long t_end, int d, float xs_mul,
-                                   float ms, bool trig, float (*xs)[DP], float* scale, int tid) {
+                                   float ms, int kind, float (*xs)[DP], float* scale, int tid) {
   for (int i = tid; i < TILE * d; i += NT) {
     const int t = i / d, c = i % d;
     const long long tok = t0 + t;
@@ -110,7 +117,9 @@ __device__ inline void load_scaled(const T* X, long long t0, long long t_end, in
   if (tid < TILE) {
     float s = 0.f;
     for (int c = 0; c < d; ++c) s = fmaf(xs[tid][c], xs[tid][c], s);
-    scale[tid] = trig ? expf(0.5f * s) * ms : ms;
+    scale[tid] = kind == KIND_TRIG  ? expf(0.5f * s) * ms
+                 : kind == KIND_POS ? 0.5f * s - logf(ms)
+                                    : ms;
   }
 }
 
@@ -163,9 +172,9 @@ __global__ __launch_bounds__(NT) void state_kernel(Args a) {
     for (long long t0 = t_begin; t0 < t_end; t0 += TILE) {
       __syncthreads();
       load_values(V, t0, t_end, d, vs, tid);
-      load_scaled(K, t0, t_end, d, xs_mul, ms, trig, ks, kscale, tid);
+      load_scaled(K, t0, t_end, d, xs_mul, ms, a.kind, ks, kscale, tid);
       __syncthreads();
-      feature_chunk(ks, kscale, om, ph, d, rc, trig, tid);
+      feature_chunk(ks, kscale, om, ph, d, rc, a.kind, tid);
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < ENT_S; ++j) {
@@ -248,11 +257,11 @@ __global__ __launch_bounds__(NT) void readout_kernel(Args a, int causal) {
   for (long long t0 = t_first; t0 < t_stop; t0 += TILE) {
     const long long t_end = min(t_stop, t0 + TILE);
     __syncthreads();
-    load_scaled(Q, t0, t_end, d, xs_mul, ms, trig, qs, qscale, tid);
+    load_scaled(Q, t0, t_end, d, xs_mul, ms, a.kind, qs, qscale, tid);
     if (causal) {
       __syncthreads();
       load_values(V, t0, t_end, d, vs, tid);
-      load_scaled(K, t0, t_end, d, xs_mul, ms, trig, ks, kscale, tid);
+      load_scaled(K, t0, t_end, d, xs_mul, ms, a.kind, ks, kscale, tid);
     }
     float o[ENT_O];
     float scv[ENT_SC];
@@ -271,8 +280,8 @@ __global__ __launch_bounds__(NT) void readout_kernel(Args a, int causal) {
         stc[fl][c] = state[(size_t)feat_index(fl, r0, rc, m, trig) * dp1 + c];
       }
       __syncthreads();
-      feature_chunk(qs, qscale, om, phq, d, rc, trig, tid);
-      if (causal) feature_chunk(ks, kscale, om, phk, d, rc, trig, tid);
+      feature_chunk(qs, qscale, om, phq, d, rc, a.kind, tid);
+      if (causal) feature_chunk(ks, kscale, om, phk, d, rc, a.kind, tid);
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < ENT_O; ++j) {

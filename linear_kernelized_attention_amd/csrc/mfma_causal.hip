@@ -67,6 +67,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     const uint16_t* __restrict__ start, uint16_t* __restrict__ out, int L, int seg_len, int n_seg,
     long long BH, float omega_scale, float knorm_scale) {
   constexpr bool TRIG = KIND == KIND_TRIG;
+  constexpr bool POS = KIND == KIND_POS;
   constexpr int M = NW * 32;
   constexpr int F = TRIG ? 2 * M : M;
   constexpr int FT = TRIG ? 4 : 2;    // feature tiles of 16 per wave
@@ -89,6 +90,10 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][CT * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][CT * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][NCOL * CROW];
+  // positive map: exponent offsets log2(e) |x~|^2 / 2 of the chunk's keys
+  // and queries
+  __shared__ __attribute__((aligned(16))) float Hk[2][CT];
+  __shared__ __attribute__((aligned(16))) float Hq[2][CT];
   // per wave: the transposed phi(K) tile, later reused for the partial out^T
   __shared__ __attribute__((aligned(16))) float Red[NW][RED_FLOATS];
   // per wave: its Omega~ fragments (2 row tiles x 2 column halves)
@@ -161,21 +166,25 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
       const bool kvtask = task >= NQT && task < NTASK;
-      float ct[2];
+      float ct[2], hs[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        // squared norms: of the keys, and (positive map) of the query chunk
+        const bool use = kvtask || (POS && h == 0 && task < NQT);
         const uint16_t* kv = (const uint16_t*)&r.d[k][h];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float x = kvtask ? bf16_to_f32(kv[i]) : 0.f;
+          const float x = use ? bf16_to_f32(kv[i]) : 0.f;
           ss = fmaf(x, x, ss);
         }
         ss = octet_sum(ss);
         ct[h] = TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f;
+        hs[h] = 0.5f * LOG2E * ss * knorm_scale;
       }
       if (task < NQT) {
         *(u32x4*)&Qs[buf][(task >> 3) * KROW + (task & 7) * 8] = r.d[k][0];
+        if (POS && (task & 7) == 0) Hq[buf][task >> 3] = hs[0];
       } else if (task < NTASK) {
         const int kv = task - NQT;
         const int q = kv >> 3, c8 = kv & 7;
@@ -185,6 +194,10 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
           if (t0 + t + h >= seg1) ct[h] = 0.f;
         *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = r.d[k][0];
         *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = r.d[k][1];
+        if (POS && c8 == 0) {
+          Hk[buf][t] = hs[0];
+          Hk[buf][t + 1] = hs[1];
+        }
         const uint16_t* v0 = (const uint16_t*)&r.d[k][2];
         const uint16_t* v1 = (const uint16_t*)&r.d[k][3];
 #pragma unroll
@@ -226,11 +239,16 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     bf16x8 fk[FT];
     {
       float sv[2][8], cv[2][8];
+      floatx4 hk[2];   // positive map: offsets of tokens 16 ts + 4 g + r
+      if (POS)
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) hk[ts] = *(const floatx4*)&Hk[buf][16 * ts + 4 * g];
 #pragma unroll
       for (int ot = 0; ot < 2; ++ot) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (TRIG) sincos_rev(PK[j >> 2][ot][j & 3], &sv[ot][j], &cv[ot][j]);
+          else if (POS) sv[ot][j] = __builtin_amdgcn_exp2f(PK[j >> 2][ot][j & 3] - hk[j >> 2][j & 3]);
           else sv[ot][j] = fmaxf(PK[j >> 2][ot][j & 3], 0.f);
         }
         fk[ot] = pack8(sv[ot]);
@@ -266,6 +284,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (TRIG) sincos_rev(PQ[j & 1][nt][j >> 1], &sv[j], &cv[j]);
+        else if (POS) sv[j] = __builtin_amdgcn_exp2f(PQ[j & 1][nt][j >> 1] - Hq[buf][16 * nt + c]);
         else sv[j] = fmaxf(PQ[j & 1][nt][j >> 1], 0.f);
       }
       bq[0][nt] = pack8(sv);
@@ -415,7 +434,7 @@ void launch_causal(const Problem& p, const Buffers& b, const CausalPlan& cp, con
 template <int KIND>
 hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
   const CausalPlan cp = plan_causal(p);
-  const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
+  const float oscale = omega_scale_for(KIND);
   uint16_t* start = (uint16_t*)((char*)b.ws + cp.keys.part_bytes);
 
   phase_begin(hook, s, "mfma_kv_state");
@@ -452,6 +471,7 @@ size_t causal_workspace_bytes(const Problem& p) {
 
 hipError_t run_causal(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
   if (p.kind == KIND_TRIG) return run_causal_kind<KIND_TRIG>(p, b, s, hook);
+  if (p.kind == KIND_POS) return run_causal_kind<KIND_POS>(p, b, s, hook);
   return run_causal_kind<KIND_RELU>(p, b, s, hook);
 }
 

@@ -33,6 +33,7 @@ __host__ __device__ inline size_t state_elems(int F) { return (size_t)F * (D + 1
 __device__ inline int vtile_off(int ft, int n) { return (ft * 4 + n) * TILE_ELEMS; }
 __device__ inline int z_off(int F, int f) { return F * D + f; }
 constexpr float INV_2PI = 0.15915494309189535f;
+constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -135,7 +136,10 @@ __device__ inline float octet_sum(float x) {
 // loaded one tile earlier; one barrier per tile separates the writes of a
 // buffer from its last reads three tiles before.
 constexpr int KV_NBUF = 3;
-constexpr size_t KV_LDS_BYTES = (size_t)KV_NBUF * (TK * KROW + NCOL * VROW) * sizeof(uint16_t);
+// per buffer: keys, transposed values, and (positive map) the tokens'
+// exponent offsets log2(e) |k~|^2 / 2
+constexpr size_t KV_LDS_BYTES =
+    (size_t)KV_NBUF * ((TK * KROW + NCOL * VROW) * sizeof(uint16_t) + TK * sizeof(float));
 
 template <int KIND, int NW>
 __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -145,6 +149,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
                                       float omega_scale, float knorm_scale, long long bh, int task,
                                       uint16_t* lds) {
   constexpr bool TRIG = KIND == KIND_TRIG;
+  constexpr bool POS = KIND == KIND_POS;
   constexpr int FT = TRIG ? 2 : 1;      // feature tiles per wave (sin, cos)
   constexpr int NT = NW * 64;
   constexpr int NTASK = TK / 2 * 8;     // (token pair, 8-column chunk) tasks
@@ -158,6 +163,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
 
   uint16_t (*Ks)[TK * KROW] = reinterpret_cast<uint16_t (*)[TK * KROW]>(lds);
   uint16_t (*Vt)[NCOL * VROW] = reinterpret_cast<uint16_t (*)[NCOL * VROW]>(lds + NBUF * TK * KROW);
+  float (*Hn)[TK] = reinterpret_cast<float (*)[TK]>(lds + NBUF * (TK * KROW + NCOL * VROW));
 
   const int seg0 = split * seg_len;
   const int seg1 = min(L, seg0 + seg_len);
@@ -226,6 +232,8 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
         }
         ss = octet_sum(ss);
         ct[h] = (t0 + t + h < seg1) ? (TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f) : 0.f;
+        // positive map: the key weight stays in the feature exponent
+        if (POS && c8 == 0 && task < NTASK) Hn[buf][t + h] = 0.5f * LOG2E * ss * knorm_scale;
       }
       if (CH * NT != NTASK && task >= NTASK) continue;
       *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = raw.k[k][0];
@@ -267,14 +275,25 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       P[ts] = mfma16(kf[ts][1], om1, p);
     }
   };
+  // the exponent offsets of the tokens of step kh (positive map): slot
+  // j = 4 ts + r <-> token 32 kh + 16 ts + 4 g + r
+  auto ld_h = [&](const float* hn, int kh, floatx4 (&h)[2]) {
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) h[ts] = *(const floatx4*)&hn[32 * kh + 16 * ts + 4 * g];
+  };
   // A fragment slot j = 4 ts + r <-> token 32 kh + 16 ts + 4 g + r
-  auto feat = [&](const floatx4 (&P)[2], bf16x8 (&fa)[FT]) {
+  auto feat = [&](const floatx4 (&P)[2], const floatx4 (&h)[2], bf16x8 (&fa)[FT]) {
     if (TRIG) {
       float sv[8], cv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) sincos_rev(P[j >> 2][j & 3], &sv[j], &cv[j]);
       fa[0] = pack8(sv);
       fa[FT - 1] = pack8(cv);
+    } else if (POS) {
+      float rv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rv[j] = __builtin_amdgcn_exp2f(P[j >> 2][j & 3] - h[j >> 2][j & 3]);
+      fa[0] = pack8(rv);
     } else {
       float rv[8];
 #pragma unroll
@@ -321,10 +340,12 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       bf16x8 vcur[5], k2[2][2], fcur[FT];
       floatx4 Pn[2];
       ld_v(vtc, s, vcur);
+      floatx4 hv[2];
+      if (POS) ld_h(Hn[i % NBUF], s, hv);
       ld_k(s < 2 ? ksc : ksn, (s + 2) & 3, k2);
       contr(fprev, vprev);
       proj(kn, Pn);
-      feat(P, fcur);
+      feat(P, hv, fcur);
       if (s == 1 && i + 2 < n_tiles) {
         stage(raw, i + 2);
         if (i + 3 < n_tiles) fetch(raw, i + 3);
@@ -384,6 +405,15 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------- key-side host
+// Scale applied to Omega before the bf16 projection: d^-1/4 (the library's
+// x~), times 1/(2 pi) for the trig map (the sine/cosine units take
+// revolutions) or log2(e) for the positive map (v_exp_f32 is 2^x); the
+// ReLU map is positively homogeneous and needs none.
+inline float omega_scale_for(int kind) {
+  const float s = powf((float)D, -0.25f);
+  return kind == KIND_TRIG ? s * INV_2PI : kind == KIND_POS ? s * LOG2E : 1.0f;
+}
+
 // Key-side partition: token splits (segments) x feature parts per head.
 struct Plan {
   int n_split, seg_len;   // token splits of the key side

@@ -97,6 +97,7 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
                                      int nsum, uint16_t* __restrict__ out, int L, long long bh,
                                      int qblock, uint16_t* smem) {
   constexpr bool TRIG = KIND == KIND_TRIG;
+  constexpr bool POS = KIND == KIND_POS;
   constexpr int M = 32 * NPAIR;
   constexpr int F = TRIG ? 2 * M : M;
   constexpr int NKS = F / 32;
@@ -120,6 +121,25 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       qf[nt][kk] = *(const bf16x8*)(Q + head + (size_t)tok * D + 32 * kk + 8 * g);
+  }
+  // positive map: the exponent offset log2(e) |q~|^2 / 2 of token
+  // t0 + 16 nt + c (the four lane groups each hold 16 of its 64 values)
+  float hq[4] = {0.f, 0.f, 0.f, 0.f};
+  if (POS) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (float)qf[nt][kk][j];
+          ss = fmaf(x, x, ss);
+        }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      hq[nt] = 0.5f * LOG2E * ss * (1.0f / 8.0f);   // |q~|^2 = |q|^2 / sqrt(64)
+    }
   }
   // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
   constexpr int NO = NOT * 2 * 64;
@@ -263,6 +283,11 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         for (int j = 0; j < 8; ++j) sincos_rev(P[j >> 2][nt][j & 3], &sv[j], &cv[j]);
         Fr[0][nt] = pack8(sv);
         Fr[FT - 1][nt] = pack8(cv);
+      } else if (POS) {
+        float rv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rv[j] = __builtin_amdgcn_exp2f(P[j >> 2][nt][j & 3] - hq[nt]);
+        Fr[0][nt] = pack8(rv);
       } else {
         float rv[8];
 #pragma unroll
@@ -399,7 +424,7 @@ size_t red_bytes(const Problem& p, const Plan& pl) {
 
 template <int KIND>
 hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
-  const float oscale = KIND == KIND_TRIG ? powf((float)D, -0.25f) * INV_2PI : 1.0f;
+  const float oscale = omega_scale_for(KIND);
   const Plan pl = plan_keys(p, 256, TK);
   uint16_t* part = (uint16_t*)b.ws;
   uint16_t* ofrag = (uint16_t*)((char*)b.ws + pl.part_bytes + red_bytes(p, pl));
@@ -449,6 +474,7 @@ size_t workspace_bytes(const Problem& p) {
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {
   if (p.causal) return run_causal(p, b, s, hook);
   if (p.kind == KIND_TRIG) return run_kind<KIND_TRIG>(p, b, s, hook);
+  if (p.kind == KIND_POS) return run_kind<KIND_POS>(p, b, s, hook);
   return run_kind<KIND_RELU>(p, b, s, hook);
 }
 

@@ -226,7 +226,7 @@ class Workload:
     d: int
     m: int
     dtype: str
-    kind: str                # "trig" | "relu"
+    kind: str                # "trig" | "relu" | "positive"
     causal: bool
     norm_shells: bool = False
     sampled_rows: Optional[int] = None   # oracle checks only these rows
@@ -246,6 +246,9 @@ WORKLOADS: Dict[str, Workload] = {
     "head": Workload("head", 4, 8, 4096, 64, 256, "bf16", "trig", False),
     "c4_bidir": Workload("c4_bidir", 1, 8, 32768, 64, 256, "bf16", "trig", False, True, 256),
     "c4_causal": Workload("c4_causal", 1, 8, 32768, 64, 256, "bf16", "trig", True, True, 256),
+    # The positive (softmax-kernel) map on the headline shape.
+    "pos_bidir": Workload("pos_bidir", 4, 8, 4096, 64, 256, "bf16", "positive", False),
+    "pos_causal": Workload("pos_causal", 4, 8, 4096, 64, 256, "bf16", "positive", True),
 }
 
 BLOCK_WORKLOAD = dict(B=2, L=4096, E=512, H=8, d=64, m=256, kind="relu", dtype="bf16")

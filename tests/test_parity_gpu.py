@@ -43,7 +43,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("kind", ["trig", "relu"])
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SMALL, ids=[f"{s[0]}x{s[1]}x{s[2]}_d{s[3]}_m{s[4]}_{s[5]}" for s in SMALL])
 def test_small_full(shape, kind, causal):
@@ -86,7 +86,7 @@ def test_config2_full(name):
         assert err <= 2e-2
 
 
-@pytest.mark.parametrize("name", ["c3_causal", "head", "c4_bidir", "c4_causal"])
+@pytest.mark.parametrize("name", ["c3_causal", "head", "c4_bidir", "c4_causal", "pos_bidir", "pos_causal"])
 def test_full_size_sampled_rows(name):
     w = I.WORKLOADS[name]
     dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype, norm_shells=w.norm_shells)
