@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
         hs[h] = 0.5f * LOG2E * ss * knorm_scale;
       }
       if (task < NQT) {
-        *(u32x4*)&Qs[buf][(task >> 3) * KROW + (task & 7) * 8] = r.d[k][0];
+        *(u32x4*)&Qs[buf][k_index(task >> 3, task & 7)] = r.d[k][0];
         if (POS && (task & 7) == 0) Hq[buf][task >> 3] = hs[0];
       } else if (task < NTASK) {
         const int kv = task - NQT;
@@ -192,8 +192,8 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           if (t0 + t + h >= seg1) ct[h] = 0.f;
-        *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = r.d[k][0];
-        *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = r.d[k][1];
+        *(u32x4*)&Ks[buf][k_index(t, c8)] = r.d[k][0];
+        *(u32x4*)&Ks[buf][k_index(t + 1, c8)] = r.d[k][1];
         if (POS && c8 == 0) {
           Hk[buf][t] = hs[0];
           Hk[buf][t + 1] = hs[1];
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     floatx4 PK[2][2];
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts) {
-      const bf16x8 k0 = *(const bf16x8*)&ks[(16 * ts + c) * KROW + 8 * g];
-      const bf16x8 k1 = *(const bf16x8*)&ks[(16 * ts + c) * KROW + 32 + 8 * g];
+      const bf16x8 k0 = *(const bf16x8*)&ks[k_index(16 * ts + c, g)];
+      const bf16x8 k1 = *(const bf16x8*)&ks[k_index(16 * ts + c, 4 + g)];
 #pragma unroll
       for (int ot = 0; ot < 2; ++ot) {
         floatx4 p = {0.f, 0.f, 0.f, 0.f};
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     floatx4 PQ[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const bf16x8 q0 = *(const bf16x8*)&qs[(16 * nt + c) * KROW + 8 * g];
-      const bf16x8 q1 = *(const bf16x8*)&qs[(16 * nt + c) * KROW + 32 + 8 * g];
+      const bf16x8 q0 = *(const bf16x8*)&qs[k_index(16 * nt + c, g)];
+      const bf16x8 q1 = *(const bf16x8*)&qs[k_index(16 * nt + c, 4 + g)];
 #pragma unroll
       for (int ot = 0; ot < 2; ++ot) {
         floatx4 p = {0.f, 0.f, 0.f, 0.f};

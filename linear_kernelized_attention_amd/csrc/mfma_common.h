@@ -5,6 +5,8 @@
 // B[8g + j][c]; C (16 x 16) lane holds C[4g + r][c], r = 0..3.
 #pragma once
 
+#include <type_traits>
+
 #include "favor_internal.h"
 
 namespace favor {
@@ -104,14 +106,20 @@ __device__ inline int pair_token(int q) {
 }
 
 constexpr int TK = 128;           // tokens per key tile (4 contraction k-steps)
-constexpr int VROW = TK + 8;      // padded LDS row of the transposed values
-constexpr int KROW = D + 8;       // padded LDS row of the keys
+constexpr int VROW = TK + 16;     // padded LDS row of the transposed values
+constexpr int KROW = D;           // LDS row of the keys (swizzled, no padding)
 
-// Element offset of (value column `row`, token slot s) in the transposed
-// value tile: 16-byte groups of 8 slots are XOR-swizzled by row / 8 so that
-// both the staging writes and the fragment reads avoid bank conflicts.
+// LDS layouts of a staged key tile, chosen by measuring ds_read_b128 and
+// ds_write cycles on gfx950 for the exact lane patterns used here (the
+// fragment reads of 16 rows x 4 chunks and the staging writes): both reads
+// run conflict-free at about 4 cycles per instruction, where the padded
+// layouts that suit a 32-bank LDS take about 7.5.
+// Keys: 16-byte chunk ch of row t sits at chunk ch ^ (t % 8) of the row.
+__device__ inline int k_index(int t, int ch) { return t * KROW + ((ch ^ (t & 7)) << 3); }
+// Transposed values: element (value column `row`, token slot s); 16-byte
+// groups of 8 slots are XOR-swizzled by row / 16 on 288-byte rows.
 __device__ inline int vt_index(int row, int s) {
-  return row * VROW + (((s >> 3) ^ ((row >> 3) & 7)) << 3) + (s & 7);
+  return row * VROW + (((s >> 3) ^ (row >> 4)) << 3) + (s & 7);
 }
 
 // Sum over the 8 lanes of an aligned lane octet (DPP, no LDS traffic).
@@ -169,6 +177,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
   const int seg1 = min(L, seg0 + seg_len);
   const size_t head = (size_t)bh * L * D;
   const int n_tiles = (seg1 - seg0 + TK - 1) / TK;
+  const float half_log2e_knorm = 0.5f * LOG2E * knorm_scale;
 
   // value rows 72..79 are padding: zero them once (rows 65..71 receive
   // copies of the z column during staging)
@@ -212,8 +221,10 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       }
     }
   };
-  auto stage = [&](const Raw& raw, int tile) {
-    const int buf = tile % NBUF;
+  // buffer index as a compile-time constant (std::integral_constant), so
+  // that every LDS address is a per-thread base plus an immediate offset
+  auto stage = [&](const Raw& raw, auto bufc, int tile) {
+    constexpr int buf = decltype(bufc)::value;
     const int t0 = seg0 + tile * TK;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
@@ -231,13 +242,15 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
           ss = fmaf(x, x, ss);
         }
         ss = octet_sum(ss);
-        ct[h] = (t0 + t + h < seg1) ? (TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f) : 0.f;
-        // positive map: the key weight stays in the feature exponent
-        if (POS && c8 == 0 && task < NTASK) Hn[buf][t + h] = 0.5f * LOG2E * ss * knorm_scale;
+        // 2^(log2(e) |k~|^2 / 2): c_t of the trig map, and (positive map)
+        // the exponent offset that stays in the feature
+        const float e2 = ss * half_log2e_knorm;
+        ct[h] = (t0 + t + h < seg1) ? (TRIG ? __builtin_amdgcn_exp2f(e2) : 1.f) : 0.f;
+        if (POS && c8 == 0 && task < NTASK) Hn[buf][t + h] = e2;
       }
       if (CH * NT != NTASK && task >= NTASK) continue;
-      *(u32x4*)&Ks[buf][t * KROW + c8 * 8] = raw.k[k][0];
-      *(u32x4*)&Ks[buf][(t + 1) * KROW + c8 * 8] = raw.k[k][1];
+      *(u32x4*)&Ks[buf][k_index(t, c8)] = raw.k[k][0];
+      *(u32x4*)&Ks[buf][k_index(t + 1, c8)] = raw.k[k][1];
       const uint16_t* v0 = (const uint16_t*)&raw.v[k][0];
       const uint16_t* v1 = (const uint16_t*)&raw.v[k][1];
 #pragma unroll
@@ -256,15 +269,15 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts) {
       const int row = 32 * kh + 16 * ts + c;
-      kf[ts][0] = *(const bf16x8*)&ks[row * KROW + 8 * g];
-      kf[ts][1] = *(const bf16x8*)&ks[row * KROW + 32 + 8 * g];
+      kf[ts][0] = *(const bf16x8*)&ks[k_index(row, g)];
+      kf[ts][1] = *(const bf16x8*)&ks[k_index(row, 4 + g)];
     }
   };
   auto ld_v = [&](const uint16_t* vt, int kh, bf16x8 (&vf)[5]) {
 #pragma unroll
     for (int n = 0; n < 5; ++n) {
       const int row = 16 * n + c;
-      vf[n] = *(const bf16x8*)&vt[row * VROW + (((4 * kh + g) ^ ((row >> 3) & 7)) << 3)];
+      vf[n] = *(const bf16x8*)&vt[vt_index(row, 8 * (4 * kh + g))];
     }
   };
   auto proj = [&](const bf16x8 (&kf)[2][2], floatx4 (&P)[2]) {
@@ -310,11 +323,14 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
 
   // prologue: load tiles 0 and 1 together, stage them, load tile 2,
   // project step 0
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   fetch(raw, 0);
-  if (n_tiles > 1) fetch(raw1, 1);
-  stage(raw, 0);
-  if (n_tiles > 2) fetch(raw, 2);
-  if (n_tiles > 1) stage(raw1, 1);
+  fetch(raw1, 1);
+  stage(raw, B0{}, 0);
+  fetch(raw, 2);
+  stage(raw1, B1{}, 1);
   __syncthreads();
 
   floatx4 P[2];
@@ -331,24 +347,31 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
 #pragma unroll
   for (int n = 0; n < 5; ++n) vprev[n] = zero8;
 
-  for (int i = 0; i < n_tiles; ++i) {
-    const uint16_t* ksc = Ks[i % NBUF];
-    const uint16_t* vtc = Vt[i % NBUF];
-    const uint16_t* ksn = Ks[(i + 1) % NBUF];
+  // One tile in buffer bufc; tile i + 2 is staged into the buffer of tile
+  // i - 1 (read for the last time before the previous barrier).  Staging
+  // and fetching run unconditionally, so that they share a basic block with
+  // the step's matrix instructions: past the segment end they stage tokens
+  // with weight 0 into a buffer that is never read again, and fetch the
+  // segment's last token (in bounds).
+  auto tile_body = [&](auto bufc, int i) {
+    constexpr int B = decltype(bufc)::value;
+    const uint16_t* ksc = Ks[B];
+    const uint16_t* vtc = Vt[B];
+    const uint16_t* ksn = Ks[(B + 1) % NBUF];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 vcur[5], k2[2][2], fcur[FT];
       floatx4 Pn[2];
       ld_v(vtc, s, vcur);
       floatx4 hv[2];
-      if (POS) ld_h(Hn[i % NBUF], s, hv);
+      if (POS) ld_h(Hn[B], s, hv);
       ld_k(s < 2 ? ksc : ksn, (s + 2) & 3, k2);
       contr(fprev, vprev);
       proj(kn, Pn);
       feat(P, hv, fcur);
-      if (s == 1 && i + 2 < n_tiles) {
-        stage(raw, i + 2);
-        if (i + 3 < n_tiles) fetch(raw, i + 3);
+      if (s == 1) {
+        stage(raw, std::integral_constant<int, (B + 2) % NBUF>{}, i + 2);
+        fetch(raw, i + 3);
       }
 #pragma unroll
       for (int ts = 0; ts < 2; ++ts) P[ts] = Pn[ts];
@@ -368,6 +391,11 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+  };
+  for (int i = 0; i < n_tiles; i += NBUF) {
+    tile_body(B0{}, i);
+    if (i + 1 < n_tiles) tile_body(B1{}, i + 1);
+    if (i + 2 < n_tiles) tile_body(B2{}, i + 2);
   }
   contr(fprev, vprev);
 
