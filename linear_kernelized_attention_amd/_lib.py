@@ -196,7 +196,8 @@ def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, pa
 
 def favor_profile_attention(q, k, v, omega, kind="trig", causal=False, path="auto", iters=20,
                             out=None, workspace=None) -> List[Tuple[str, float]]:
-    """[(kernel name, mean ms per call)] measured with HIP events."""
+    """[(kernel name, mean ms per launch)]: each kernel launched `iters`
+    times back-to-back between two HIP events on the current stream."""
     args, out, _ = _call_args(q, k, v, omega, kind, causal, path, out, workspace)
     max_ph = 8
     ms = (ctypes.c_float * max_ph)()

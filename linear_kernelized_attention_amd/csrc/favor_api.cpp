@@ -222,7 +222,8 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
   *n_phases = 0;
   if (c.empty) return FAVOR_OK;
   hipStream_t s = (hipStream_t)stream;
-  std::vector<hipEvent_t> ev((size_t)iters * 2 * max_phases, nullptr);
+  std::vector<hipEvent_t> ev((size_t)2 * max_phases, nullptr);
+  std::vector<int> reps_used(max_phases, 1);
   int rc = FAVOR_OK;
   for (auto& e : ev) {
     if (hipEventCreate(&e) != hipSuccess) { e = nullptr; rc = FAVOR_ERR_HIP; break; }
@@ -230,30 +231,20 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
   int phases = 0;
   std::vector<double> sum(max_phases, 0.0);
   if (rc == FAVOR_OK) {
-    for (int it = 0; it < iters && rc == FAVOR_OK; ++it) {
-      favor::PhaseHook hook{ev.data() + (size_t)it * 2 * max_phases, max_phases, 0,
-                            it == 0 ? names : nullptr};
-      rc = launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, s, &hook);
-      phases = hook.n;
-    }
+    favor::PhaseHook hook{ev.data(), max_phases, 0, names, iters, reps_used.data()};
+    rc = launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, s, &hook);
+    phases = hook.n;
     if (rc == FAVOR_OK && hipStreamSynchronize(s) != hipSuccess) rc = FAVOR_ERR_HIP;
-    if (rc == FAVOR_OK) {
-      for (int it = 0; it < iters && rc == FAVOR_OK; ++it)
-        for (int ph = 0; ph < phases; ++ph) {
-          float ms = 0.f;
-          const size_t base = (size_t)it * 2 * max_phases;
-          if (hipEventElapsedTime(&ms, ev[base + 2 * ph], ev[base + 2 * ph + 1]) != hipSuccess) {
-            rc = FAVOR_ERR_HIP;
-            break;
-          }
-          sum[ph] += ms;
-        }
+    for (int ph = 0; ph < phases && rc == FAVOR_OK; ++ph) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[2 * ph], ev[2 * ph + 1]) != hipSuccess) rc = FAVOR_ERR_HIP;
+      sum[ph] = (double)ms / reps_used[ph];
     }
   }
   for (auto& e : ev)
     if (e) hipEventDestroy(e);
   if (rc != FAVOR_OK) return rc;
-  for (int ph = 0; ph < phases; ++ph) phase_ms[ph] = (float)(sum[ph] / iters);
+  for (int ph = 0; ph < phases; ++ph) phase_ms[ph] = (float)sum[ph];
   *n_phases = phases;
   return FAVOR_OK;
 }

@@ -29,12 +29,19 @@ struct Buffers {
 };
 
 // Optional per-kernel event recording (used by favor_profile_attention).
+// A phase whose kernels are a pure function of the inputs and of earlier
+// phases' workspace is launched `reps` times back-to-back between its two
+// events (phase_reps), so that the events time steady-state launches.
 struct PhaseHook {
   hipEvent_t* ev;  // 2 * max_phases events: begin/end of each phase
   int max_phases;
   int n;
   char* names;     // max_phases * 48 bytes, may be null
+  int reps;        // launches per repeatable phase
+  int* reps_used;  // max_phases entries: launches made by each phase
 };
+
+inline int phase_reps(const PhaseHook* h) { return h && h->reps > 1 ? h->reps : 1; }
 
 inline void phase_begin(PhaseHook* h, hipStream_t s, const char* name) {
   if (!h || h->n >= h->max_phases) return;
@@ -47,9 +54,10 @@ inline void phase_begin(PhaseHook* h, hipStream_t s, const char* name) {
   }
 }
 
-inline void phase_end(PhaseHook* h, hipStream_t s) {
+inline void phase_end(PhaseHook* h, hipStream_t s, int reps = 1) {
   if (!h || h->n >= h->max_phases) return;
   (void)hipEventRecord(h->ev[2 * h->n + 1], s);
+  if (h->reps_used) h->reps_used[h->n] = reps;
   ++h->n;
 }
 

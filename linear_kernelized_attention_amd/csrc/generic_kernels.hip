@@ -388,25 +388,31 @@ hipError_t run_typed(const Problem& p, const Buffers& b, hipStream_t s, PhaseHoo
   a.seg_len = pl.seg_len; a.n_seg = pl.n_seg;
   const long long n = p.BH * (long long)p.F * (p.d + 1);
 
+  // every phase but the in-place scan may be repeated under profiling
+  const int reps = phase_reps(hook);
   phase_begin(hook, s, "generic_state");
-  hipLaunchKernelGGL(state_kernel<T>, head_grid(pl.n_seg, p.BH), dim3(NT), 0, s, a);
-  phase_end(hook, s);
+  for (int r = 0; r < reps; ++r)
+    hipLaunchKernelGGL(state_kernel<T>, head_grid(pl.n_seg, p.BH), dim3(NT), 0, s, a);
+  phase_end(hook, s, reps);
   const unsigned nb = (unsigned)((n + NT - 1) / NT);
   if (p.causal) {
     phase_begin(hook, s, "generic_scan");
     hipLaunchKernelGGL(scan_kernel, dim3(nb), dim3(NT), 0, s, a.part, n, pl.n_seg);
     phase_end(hook, s);
     phase_begin(hook, s, "generic_readout_causal");
-    hipLaunchKernelGGL(readout_kernel<T>, head_grid(pl.n_seg, p.BH), dim3(NT), 0, s, a, 1);
-    phase_end(hook, s);
+    for (int r = 0; r < reps; ++r)
+      hipLaunchKernelGGL(readout_kernel<T>, head_grid(pl.n_seg, p.BH), dim3(NT), 0, s, a, 1);
+    phase_end(hook, s, reps);
   } else {
     phase_begin(hook, s, "generic_reduce");
-    hipLaunchKernelGGL(reduce_kernel, dim3(nb), dim3(NT), 0, s, a.part, a.total, n, pl.n_seg);
-    phase_end(hook, s);
+    for (int r = 0; r < reps; ++r)
+      hipLaunchKernelGGL(reduce_kernel, dim3(nb), dim3(NT), 0, s, a.part, a.total, n, pl.n_seg);
+    phase_end(hook, s, reps);
     const int tiles = (p.L + TILE - 1) / TILE;
     phase_begin(hook, s, "generic_readout");
-    hipLaunchKernelGGL(readout_kernel<T>, head_grid(tiles, p.BH), dim3(NT), 0, s, a, 0);
-    phase_end(hook, s);
+    for (int r = 0; r < reps; ++r)
+      hipLaunchKernelGGL(readout_kernel<T>, head_grid(tiles, p.BH), dim3(NT), 0, s, a, 0);
+    phase_end(hook, s, reps);
   }
   return hipGetLastError();
 }

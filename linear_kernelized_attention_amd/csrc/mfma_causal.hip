@@ -437,18 +437,20 @@ hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, Ph
   const float oscale = omega_scale_for(KIND);
   uint16_t* start = (uint16_t*)((char*)b.ws + cp.keys.part_bytes);
 
+  const int reps = phase_reps(hook);
   phase_begin(hook, s, "mfma_kv_state");
-  launch_kv_nw<KIND>(p, b, cp.keys, nullptr, s, oscale);
-  phase_end(hook, s);
+  for (int r = 0; r < reps; ++r) launch_kv_nw<KIND>(p, b, cp.keys, nullptr, s, oscale);
+  phase_end(hook, s, reps);
 
   const long long per_seg8 = p.BH * (long long)state_elems(p.F) / 8;
   phase_begin(hook, s, "mfma_state_scan");
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s,
-                     (const uint16_t*)b.ws, start, cp.keys.n_split, per_seg8);
-  phase_end(hook, s);
+  for (int r = 0; r < reps; ++r)
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)b.ws, start, cp.keys.n_split, per_seg8);
+  phase_end(hook, s, reps);
 
   phase_begin(hook, s, "mfma_causal_chunks");
-  switch (p.m / 32) {
+  for (int r = 0; r < reps; ++r) switch (p.m / 32) {
     case 1: launch_causal<KIND, 1>(p, b, cp, start, s, oscale); break;
     case 2: launch_causal<KIND, 2>(p, b, cp, start, s, oscale); break;
     case 3: launch_causal<KIND, 3>(p, b, cp, start, s, oscale); break;
@@ -458,7 +460,7 @@ hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, Ph
     case 7: launch_causal<KIND, 7>(p, b, cp, start, s, oscale); break;
     default: launch_causal<KIND, 8>(p, b, cp, start, s, oscale); break;
   }
-  phase_end(hook, s);
+  phase_end(hook, s, reps);
   return hipGetLastError();
 }
 

@@ -430,9 +430,10 @@ hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook
   uint16_t* ofrag = (uint16_t*)((char*)b.ws + pl.part_bytes + red_bytes(p, pl));
   const long long stride = (long long)split_stride_elems(p);
 
+  const int reps = phase_reps(hook);
   phase_begin(hook, s, "mfma_kv_state");
-  launch_kv_nw<KIND>(p, b, pl, ofrag, s, oscale);
-  phase_end(hook, s);
+  for (int r = 0; r < reps; ++r) launch_kv_nw<KIND>(p, b, pl, ofrag, s, oscale);
+  phase_end(hook, s, reps);
 
   const uint16_t* src = part;
   int nsum = pl.n_split;
@@ -440,16 +441,17 @@ hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook
     uint16_t* red = (uint16_t*)((char*)b.ws + pl.part_bytes);
     const long long per8 = stride / 8;
     phase_begin(hook, s, "mfma_split_sum");
-    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((per8 + 255) / 256)), dim3(256), 0, s,
-                       (const uint16_t*)part, red, pl.n_split, per8);
-    phase_end(hook, s);
+    for (int r = 0; r < reps; ++r)
+      hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((per8 + 255) / 256)), dim3(256), 0, s,
+                         (const uint16_t*)part, red, pl.n_split, per8);
+    phase_end(hook, s, reps);
     src = red;
     nsum = 1;
   }
 
   phase_begin(hook, s, "mfma_readout");
-  launch_readout_m<KIND>(p, b, src, stride, nsum, ofrag, s);
-  phase_end(hook, s);
+  for (int r = 0; r < reps; ++r) launch_readout_m<KIND>(p, b, src, stride, nsum, ofrag, s);
+  phase_end(hook, s, reps);
   return hipGetLastError();
 }
 
