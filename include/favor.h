@@ -144,8 +144,8 @@ int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, i
  * favor_profile_attention -- per-kernel timing of favor_attention_ex.
  * Enqueues one call on `stream` in which every kernel (phase) whose result
  * depends only on the inputs and on earlier phases is launched `iters`
- * times back-to-back between a pair of HIP events (the generic path's
- * in-place scan once), waits, and writes the mean duration of one launch
+ * times back-to-back between a pair of HIP events (the generic causal
+ * scan and readout, which update state in place, once), waits, and writes the mean duration of one launch
  * of each phase in milliseconds to phase_ms[0 .. *n_phases-1] and a short
  * name of each into names (max_phases entries of 48 bytes, NUL-terminated;
  * may be null).  `out` receives the call's result.  Creates and destroys

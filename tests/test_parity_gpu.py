@@ -147,3 +147,17 @@ def test_profile_reports_kernels():
     for path in _paths(1, 2, 512, 64, 256, "bf16", "trig", False):
         phases = F.favor_profile_attention(*dev, kind="trig", path=path, iters=3)
         assert phases and all(ms > 0 for _, ms in phases)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["trig", "relu"])
+def test_profile_output_matches_call(kind, causal):
+    # favor_profile_attention repeats kernels back-to-back; its output must
+    # still be the call's result (no phase may be repeated on its own output)
+    dev, _, _ = problem(1, 2, 300, 64, 256, "bf16", seed=9)
+    for path in _paths(1, 2, 300, 64, 256, "bf16", kind, causal):
+        ref = F.favor_attention(*dev, kind=kind, causal=causal, path=path)
+        out = torch.empty_like(ref)
+        F.favor_profile_attention(*dev, kind=kind, causal=causal, path=path, iters=4, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int16), out.view(torch.int16)), path
