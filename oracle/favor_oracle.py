@@ -49,6 +49,20 @@ definitions state):
    of the same section with exp(q.k/sqrt(d)) replaced by phi(q).phi(k).
 6. Textbook softmax attention D^-1 exp(Q K^T / sqrt(d)) V
    [blog §核心机制：FAVOR+], the large-m limit of 3 and 4.
+7. Gradients of 3 and 4 (the pages claim training-time speedups [en
+   §Methodology] but print no backward pass; this is the chain rule of
+   the same computation).  For a loss with dL/d out_i = g_i:
+     a_i = g_i / den_i,  b_i = -(g_i . out_i) / den_i     (dL/dnum, dL/dden)
+     dphi(q_i) = S_i a_i + z_i b_i
+     R_j = sum_{i >= j} phi(q_i) a_i^T,  r_j = sum_{i >= j} phi(q_i) b_i
+           (all i for bidirectional: R = dL/dS, r = dL/dz)
+     dv_j = R_j^T phi(k_j),  dphi(k_j) = R_j v_j + r_j
+   and through each map (mu = m**-0.5, x~ = d**-0.25 x, upstream w):
+     trig:     dP = c mu (w_sin cos P - w_cos sin P),  c = exp(|x~|^2/2);
+               dx~ = Omega^T dP + (w . phi) x~
+     relu:     dP = mu w [P > 0];  dx~ = Omega^T dP
+     positive: dP = w * phi;  dx~ = Omega^T dP - (w . phi) x~
+     dx = d**-0.25 dx~.
 
 Readings where the pages are silent (each is listed with its reason in
 the design notes): d**-0.25 is applied inside phi to the tensors passed
@@ -256,6 +270,111 @@ def softmax_attention(Q, K, V, causal: bool = False) -> np.ndarray:
         L = A.shape[-1]
         A = A * np.tril(np.ones((L, L)))
     return (A @ np.asarray(V, dtype=np.float64)) / A.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------- step 7
+def feature_map_vjp(X: np.ndarray, Omega: np.ndarray, kind: str, dphi: np.ndarray) -> np.ndarray:
+    """dL/dX given dL/dphi(X) = dphi (X [..., L, d], dphi [..., L, F]):
+    the chain rule through x~ = d^-1/4 x, P = x~ Omega^T and the map.
+    ReLU takes derivative 0 at P = 0."""
+    X = np.asarray(X, dtype=np.float64)
+    Omega = np.asarray(Omega, dtype=np.float64)
+    w = np.asarray(dphi, dtype=np.float64)
+    d = X.shape[-1]
+    m = Omega.shape[0]
+    mu = m ** -0.5
+    Xt = X * d ** -0.25
+    P = Xt @ Omega.T
+    if kind == "trig":
+        c = np.exp(0.5 * np.sum(Xt * Xt, axis=-1, keepdims=True))
+        ws, wc = w[..., :m], w[..., m:]
+        dP = c * mu * (ws * np.cos(P) - wc * np.sin(P))
+        phi = c * mu * np.concatenate([np.sin(P), np.cos(P)], axis=-1)
+        dXt = dP @ Omega + np.sum(w * phi, axis=-1, keepdims=True) * Xt
+    elif kind == "relu":
+        dP = mu * w * (P > 0.0)
+        dXt = dP @ Omega
+    elif kind == "positive":
+        phi = mu * np.exp(P - 0.5 * np.sum(Xt * Xt, axis=-1, keepdims=True))
+        dP = w * phi
+        dXt = dP @ Omega - np.sum(dP, axis=-1, keepdims=True) * Xt
+    else:
+        raise ValueError(f"unknown feature kind {kind!r}")
+    return dXt * d ** -0.25
+
+
+def _bidirectional_head_grad(q, k, v, g, Omega, kind):
+    phq = feature_map(q, Omega, kind)
+    phk = feature_map(k, Omega, kind)
+    S = phk.T @ v
+    z = phk.sum(axis=0)
+    den = phq @ z
+    out = (phq @ S) / den[:, None]
+    a = g / den[:, None]
+    b = -np.sum(g * out, axis=1) / den
+    dphq = a @ S.T + b[:, None] * z[None, :]
+    R = phq.T @ a                 # dL/dS  [F, d]
+    r = phq.T @ b                 # dL/dz  [F]
+    dv = phk @ R
+    dphk = v @ R.T + r[None, :]
+    return feature_map_vjp(q, Omega, kind, dphq), feature_map_vjp(k, Omega, kind, dphk), dv
+
+
+def _causal_head_grad(q, k, v, g, Omega, kind, block=64):
+    phq = feature_map(q, Omega, kind)
+    phk = feature_map(k, Omega, kind)
+    L, F = phk.shape
+    d = v.shape[1]
+    a = np.empty((L, d))
+    b = np.empty(L)
+    dphq = np.empty((L, F))
+    # forward prefix states S_i, z_i (inclusive), block by block
+    S = np.zeros((F, d))
+    z = np.zeros(F)
+    for t0 in range(0, L, block):
+        t1 = min(L, t0 + block)
+        Si = S + np.cumsum(phk[t0:t1, :, None] * v[t0:t1, None, :], axis=0)
+        zi = z + np.cumsum(phk[t0:t1], axis=0)
+        den = np.einsum("tf,tf->t", phq[t0:t1], zi)
+        out = np.einsum("tf,tfd->td", phq[t0:t1], Si) / den[:, None]
+        a[t0:t1] = g[t0:t1] / den[:, None]
+        b[t0:t1] = -np.sum(g[t0:t1] * out, axis=1) / den
+        dphq[t0:t1] = np.einsum("tfd,td->tf", Si, a[t0:t1]) + zi * b[t0:t1, None]
+        S, z = Si[-1], zi[-1]
+    # suffix sums R_j = sum_{i >= j} phi(q_i) a_i^T, r_j likewise, from the end
+    dv = np.empty((L, d))
+    dphk = np.empty((L, F))
+    R = np.zeros((F, d))
+    r = np.zeros(F)
+    for t1 in range(L, 0, -block):
+        t0 = max(0, t1 - block)
+        Rj = R + np.cumsum((phq[t0:t1, :, None] * a[t0:t1, None, :])[::-1], axis=0)[::-1]
+        rj = r + np.cumsum((phq[t0:t1] * b[t0:t1, None])[::-1], axis=0)[::-1]
+        dv[t0:t1] = np.einsum("tfd,tf->td", Rj, phk[t0:t1])
+        dphk[t0:t1] = np.einsum("tfd,td->tf", Rj, v[t0:t1]) + rj
+        R, r = Rj[0], rj[0]
+    return feature_map_vjp(q, Omega, kind, dphq), feature_map_vjp(k, Omega, kind, dphk), dv
+
+
+def favor_attention_grad(Q, K, V, Omega, dOut, kind: str = "trig", causal: bool = False,
+                         workers: Optional[int] = None):
+    """(dQ, dK, dV) of L = sum(dOut * favor_attention(Q, K, V)) on [..., L, d]
+    inputs (float64); Omega is fixed."""
+    if kind not in KINDS:
+        raise ValueError(f"unknown feature kind {kind!r}")
+    Q, K, V, G = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dOut))
+    lead = Q.shape[:-2]
+    L, d = Q.shape[-2:]
+    q2, k2, v2, g2 = (x.reshape(-1, L, d) for x in (Q, K, V, G))
+    fn = _causal_head_grad if causal else _bidirectional_head_grad
+    n = q2.shape[0]
+    res = [None] * n
+    if workers and workers > 1 and n > 1:
+        with ThreadPoolExecutor(max_workers=min(workers, n)) as ex:
+            res = list(ex.map(lambda i: fn(q2[i], k2[i], v2[i], g2[i], Omega, kind), range(n)))
+    else:
+        res = [fn(q2[i], k2[i], v2[i], g2[i], Omega, kind) for i in range(n)]
+    return tuple(np.stack([r_[j] for r_ in res]).reshape(*lead, L, d) for j in range(3))
 
 
 # ------------------------------------------------ masked-LM attention block
