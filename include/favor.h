@@ -158,6 +158,41 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
                             int* n_phases);
 
 /*
+ * favor_attention_backward -- gradients of FAVOR attention.
+ * The pages claim training-time speed-ups ("Masked Language Modeling for
+ * Proteins ..." summary pages, Methodology) but print no backward pass;
+ * this is the exact gradient of the computation favor_attention performs
+ * (blog page "用随机特征“骗”过 softmax...", section 核心机制：FAVOR+),
+ * the linear-order forms included.  For L = sum dOut . out it writes
+ *   dQ = dL/dQ, dK = dL/dK, dV = dL/dV
+ * with Omega fixed (no gradient).  With a_i = dOut_i / den_i and
+ * b_i = -(dOut_i . out_i) / den_i: dphi(q_i) = S_i a_i + z_i b_i;
+ * R_j = sum over queries i >= j (causal) or all i of phi(q_i) [a_i, b_i]^T;
+ * dV_j = R_j[:, :d]^T phi(k_j) and dphi(k_j) = R_j [v_j, 1]; then the
+ * chain rule through each feature map and x~ = d^-1/4 x.  The ReLU
+ * derivative at 0 is 0; rows that are 0/0 in the forward give NaN.
+ *   Q, K, V, dOut: [B, H, L, d] contiguous, dtype (read only).
+ *   Omega: [m, d] float32 (read only).
+ *   dQ, dK, dV: [B, H, L, d] contiguous, dtype (written; each element
+ *   once, rounded to nearest even for bf16).  They must not overlap each
+ *   other, any input or the workspace (FAVOR_ERR_ALIAS).
+ *   workspace: device memory of at least
+ *   favor_attention_backward_workspace_bytes(...) bytes, contents
+ *   ignored and overwritten; float32 state, [a, b] and suffix buffers.
+ * Every pointer is 16-byte aligned device memory owned by the caller.
+ * Runs on the generic kernel family (float32 arithmetic; d <= 64,
+ * m <= 1024, any L); other shapes return FAVOR_ERR_UNSUPPORTED.  All
+ * checks run before anything is enqueued; execution is asynchronous on
+ * `stream`.  B * H * L == 0 is a no-op.
+ */
+size_t favor_attention_backward_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
+                                                int kind, int causal);
+int favor_attention_backward(const void* Q, const void* K, const void* V, const float* Omega,
+                             const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L,
+                             int d, int m, int dtype, int kind, int causal, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Masked-LM attention block helpers (bf16), for the Performer block whose
  * attention is FAVOR ("Masked Language Modeling for Proteins ..." summary
  * pages, Methodology / 实验设计: protein sequences, multi-head attention).

@@ -33,6 +33,7 @@ EXPORTS = (
     "favor_attention_workspace_bytes", "favor_attention_workspace_bytes_ex",
     "favor_attention", "favor_attention_ex", "favor_attention_resolve_path",
     "favor_profile_attention", "favor_embed_bf16", "favor_linear_bf16",
+    "favor_attention_backward_workspace_bytes", "favor_attention_backward",
 )
 
 
@@ -61,6 +62,8 @@ def _declare(lib: ctypes.CDLL) -> None:
         "favor_profile_attention": (i, [p, p, p, p, p] + [i] * 8 + [p, z, p, i, i, p, p, i, p]),
         "favor_embed_bf16": (i, [p, p, p, i, i, i, p]),
         "favor_linear_bf16": (i, [p, p, p, i, i, i, i, i, i, p]),
+        "favor_attention_backward_workspace_bytes": (z, [i] * 8),
+        "favor_attention_backward": (i, [p] * 8 + [i] * 8 + [p, z, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -192,6 +195,41 @@ def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, pa
     args, out, _ = _call_args(q, k, v, omega, kind, causal, path, out, workspace)
     _check(lib().favor_attention_ex(*args), "favor_attention")
     return out
+
+
+def favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="trig",
+                                             causal=False) -> int:
+    return int(lib().favor_attention_backward_workspace_bytes(
+        B, H, L, d, m, DTYPE[dtype], KIND[kind], int(bool(causal))))
+
+
+def favor_attention_backward(q, k, v, omega, dout, kind: str = "trig", causal: bool = False,
+                             workspace=None, grads=None):
+    """(dq, dk, dv) of sum(dout * favor_attention(q, k, v)) on the GPU; grads
+    may supply the three output tensors."""
+    import torch
+    _validate(q, k, v, omega)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous tensor like q")
+    B, H, L, d = q.shape
+    m = omega.shape[0]
+    dt = _torch_dtype_code(q)
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    for t in grads:
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("grads must be contiguous tensors like q")
+    need = int(lib().favor_attention_backward_workspace_bytes(B, H, L, d, m, dt, KIND[kind],
+                                                              int(bool(causal))))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = grads
+    _check(lib().favor_attention_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, m, dt, KIND[kind],
+        int(bool(causal)), workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device)),
+        "favor_attention_backward")
+    return dq, dk, dv
 
 
 def favor_profile_attention(q, k, v, omega, kind="trig", causal=False, path="auto", iters=20,

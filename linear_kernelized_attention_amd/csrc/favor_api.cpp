@@ -15,7 +15,7 @@ using favor::Problem;
 
 namespace {
 
-constexpr int kVersion = (0 << 16) | (3 << 8) | 0;
+constexpr int kVersion = (0 << 16) | (4 << 8) | 0;
 constexpr int kMaxD = 64;
 constexpr int kMaxM = 1024;
 
@@ -118,6 +118,45 @@ int launch(const Checked& c, const void* Q, const void* K, const void* V, const 
   if (hipPeekAtLastError() != hipSuccess) {
     (void)hipGetLastError();
     return FAVOR_ERR_HIP;
+  }
+  return FAVOR_OK;
+}
+
+// Backward: the forward checks, plus dOut and the three gradient outputs,
+// which must not overlap any input, each other or the workspace.
+int check_backward(const void* Q, const void* K, const void* V, const float* Omega,
+                   const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L, int d,
+                   int m, int dtype, int kind, int causal, void* ws, size_t ws_bytes_given,
+                   Checked* c) {
+  int st = check_problem(B, H, L, d, m, dtype, kind, causal, &c->p, &c->empty);
+  if (st != FAVOR_OK) return st;
+  c->path = FAVOR_PATH_GENERIC;
+  if (c->empty) return FAVOR_OK;
+  if (!Q || !K || !V || !Omega || !dOut || !dQ || !dK || !dV) return FAVOR_ERR_INVALID_ARG;
+  const void* al[] = {Q, K, V, Omega, dOut, dQ, dK, dV};
+  for (const void* x : al)
+    if (!aligned16(x)) return FAVOR_ERR_INVALID_ARG;
+  if (ws && !aligned16(ws)) return FAVOR_ERR_INVALID_ARG;
+  if (!favor::generic::supports(c->p)) return FAVOR_ERR_UNSUPPORTED;
+  const size_t need = favor::generic::backward_workspace_bytes(c->p);
+  if (need > 0 && (!ws || ws_bytes_given < need)) return FAVOR_ERR_WORKSPACE;
+  const size_t esz = dtype == FAVOR_DTYPE_F32 ? 4 : 2;
+  const size_t tensor = (size_t)c->p.BH * (size_t)L * (size_t)d * esz;
+  const size_t omega_b = (size_t)m * d * sizeof(float);
+  const void* in[] = {Q, K, V, dOut};
+  void* outs[] = {dQ, dK, dV};
+  for (int i = 0; i < 3; ++i) {
+    for (const void* x : in)
+      if (overlaps(outs[i], tensor, x, tensor)) return FAVOR_ERR_ALIAS;
+    if (overlaps(outs[i], tensor, Omega, omega_b)) return FAVOR_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tensor, outs[j], tensor)) return FAVOR_ERR_ALIAS;
+    if (need > 0 && overlaps(ws, need, outs[i], tensor)) return FAVOR_ERR_ALIAS;
+  }
+  if (need > 0) {
+    for (const void* x : in)
+      if (overlaps(ws, need, x, tensor)) return FAVOR_ERR_ALIAS;
+    if (overlaps(ws, need, Omega, omega_b)) return FAVOR_ERR_ALIAS;
   }
   return FAVOR_OK;
 }
@@ -282,6 +321,34 @@ int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K
   hipError_t e = favor::block::linear((const uint16_t*)X, (const uint16_t*)W, (uint16_t*)Y, M, N, K,
                                       in_heads, out_heads, seq_len, (hipStream_t)stream);
   return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+size_t favor_attention_backward_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
+                                                int kind, int causal) {
+  Problem p;
+  bool empty;
+  if (check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty) != FAVOR_OK) return 0;
+  if (empty || !favor::generic::supports(p)) return 0;
+  return favor::generic::backward_workspace_bytes(p);
+}
+
+int favor_attention_backward(const void* Q, const void* K, const void* V, const float* Omega,
+                             const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L,
+                             int d, int m, int dtype, int kind, int causal, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Checked c;
+  int st = check_backward(Q, K, V, Omega, dOut, dQ, dK, dV, B, H, L, d, m, dtype, kind, causal,
+                          workspace, workspace_bytes, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  favor::Buffers b{Q, K, V, Omega, nullptr, workspace, workspace_bytes};
+  favor::BwdBuffers g{dOut, dQ, dK, dV};
+  if (favor::generic::run_backward(c.p, b, g, (hipStream_t)stream, nullptr) != hipSuccess)
+    return FAVOR_ERR_HIP;
+  if (hipPeekAtLastError() != hipSuccess) {
+    (void)hipGetLastError();
+    return FAVOR_ERR_HIP;
+  }
+  return FAVOR_OK;
 }
 
 }  // extern "C"

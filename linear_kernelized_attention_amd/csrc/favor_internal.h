@@ -63,10 +63,21 @@ inline void phase_end(PhaseHook* h, hipStream_t s, int reps = 1) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Gradient buffers of the backward pass (device pointers, the input dtype).
+struct BwdBuffers {
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+};
+
 namespace generic {
 bool supports(const Problem& p);
 size_t workspace_bytes(const Problem& p);
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
+                        PhaseHook* hook);
 }  // namespace generic
 
 namespace mfma {

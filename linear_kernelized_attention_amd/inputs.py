@@ -47,6 +47,7 @@ STREAM: Dict[str, int] = {
     "rows": 12,      # sampled output rows for long-sequence checks
     "qnorm": 13,     # row radii for the norm-shell distribution (queries)
     "knorm": 14,     # row radii for the norm-shell distribution (keys)
+    "dout": 15,      # upstream gradient of the output (backward pass)
 }
 
 DTYPES = ("f32", "bf16")
@@ -164,6 +165,13 @@ def attention_inputs(B: int, H: int, L: int, d: int, dtype: str, seed: int = 0,
     ks, k64 = to_storage(k, dtype)
     vs, v64 = to_storage(v, dtype)
     return AttentionInputs(B, H, L, d, dtype, qs, ks, vs, q64, k64, v64)
+
+
+def output_grads(B: int, H: int, L: int, d: int, dtype: str, seed: int = 0):
+    """dL/d out of shape [B, H, L, d]: i.i.d. N(0, 1), stored like the
+    inputs; returns (stored array, exact float64 view)."""
+    g = rng(seed, "dout").standard_normal((B, H, L, d))
+    return to_storage(g, dtype)
 
 
 def sample_rows(L: int, n: int = 256, seed: int = 0) -> np.ndarray:

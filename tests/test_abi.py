@@ -145,3 +145,39 @@ def test_host_orf_rejects_degenerate_block():
     g = np.zeros((1, 4, 4))
     with pytest.raises(F.FavorError):
         F.favor_orf_omega(g, np.ones(4), 4)
+
+
+# ------------------------------------------------------------- backward
+GA, DQA, DKA, DVA = (0x100000 * i for i in range(7, 11))
+
+
+def bcall(q=QA, k=KA, v=VA, w=WA, g=GA, dq=DQA, dk=DKA, dv=DVA, B_=2, H=2, L=64, d=64, m=256,
+          dt=1, kind=0, causal=0, ws=WS, wsb=1 << 40):
+    return F.lib().favor_attention_backward(q, k, v, w, g, dq, dk, dv, B_, H, L, d, m, dt, kind,
+                                            causal, ws, wsb, None)
+
+
+def test_backward_argument_checks():
+    assert bcall(g=0) == B.FAVOR_ERR_INVALID_ARG
+    assert bcall(dk=0) == B.FAVOR_ERR_INVALID_ARG
+    assert bcall(kind=7) == B.FAVOR_ERR_INVALID_ARG
+    assert bcall(dv=DVA + 8) == B.FAVOR_ERR_INVALID_ARG      # misaligned
+    assert bcall(d=128) == B.FAVOR_ERR_UNSUPPORTED
+    assert bcall(ws=0) == B.FAVOR_ERR_WORKSPACE
+    need = F.favor_attention_backward_workspace_bytes(2, 2, 64, 64, 256, "bf16", "trig", False)
+    assert need > 0 and bcall(wsb=need - 1) == B.FAVOR_ERR_WORKSPACE
+    assert bcall(q=0, k=0, v=0, w=0, g=0, dq=0, dk=0, dv=0, ws=0, wsb=0, L=0) == B.FAVOR_OK
+
+
+def test_backward_alias_checks():
+    assert bcall(dq=QA) == B.FAVOR_ERR_ALIAS          # output over an input
+    assert bcall(dk=GA + 64) == B.FAVOR_ERR_ALIAS     # output over dOut
+    assert bcall(dv=DKA) == B.FAVOR_ERR_ALIAS         # outputs overlap each other
+    assert bcall(ws=DQA) == B.FAVOR_ERR_ALIAS         # workspace over an output
+
+
+def test_backward_workspace_covers_forward_state():
+    for causal in (False, True):
+        fwd = F.favor_attention_workspace_bytes(1, 8, 4096, 64, 256, "bf16", "trig", causal, "generic")
+        bwd = F.favor_attention_backward_workspace_bytes(1, 8, 4096, 64, 256, "bf16", "trig", causal)
+        assert bwd > fwd
