@@ -180,17 +180,28 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
  *   favor_attention_backward_workspace_bytes(...) bytes, contents
  *   ignored and overwritten; float32 state, [a, b] and suffix buffers.
  * Every pointer is 16-byte aligned device memory owned by the caller.
- * Runs on the generic kernel family (float32 arithmetic; d <= 64,
- * m <= 1024, any L); other shapes return FAVOR_ERR_UNSUPPORTED.  All
- * checks run before anything is enqueued; execution is asynchronous on
- * `stream`.  B * H * L == 0 is a no-op.
+ * Kernel families: MFMA (bf16, d = 64, m a multiple of 32 up to 256,
+ * bidirectional; the forward's kernels plus a fused feature-gradient
+ * kernel) and generic (float32 arithmetic; d <= 64, m <= 1024, any L, both
+ * directions).  favor_attention_backward picks MFMA when it applies; the
+ * _ex variants take a favor_path as for the forward (FAVOR_ERR_UNSUPPORTED
+ * if the requested family cannot run the problem).  All checks run before
+ * anything is enqueued; execution is asynchronous on `stream`.
+ * B * H * L == 0 is a no-op.  The workspace size query returns 0 for an
+ * invalid or unsupported request.
  */
 size_t favor_attention_backward_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
                                                 int kind, int causal);
+size_t favor_attention_backward_workspace_bytes_ex(int B, int H, int L, int d, int m, int dtype,
+                                                   int kind, int causal, int path);
 int favor_attention_backward(const void* Q, const void* K, const void* V, const float* Omega,
                              const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L,
                              int d, int m, int dtype, int kind, int causal, void* workspace,
                              size_t workspace_bytes, void* stream);
+int favor_attention_backward_ex(const void* Q, const void* K, const void* V, const float* Omega,
+                                const void* dOut, void* dQ, void* dK, void* dV, int B, int H,
+                                int L, int d, int m, int dtype, int kind, int causal,
+                                void* workspace, size_t workspace_bytes, void* stream, int path);
 
 /*
  * Masked-LM attention block helpers (bf16), for the Performer block whose

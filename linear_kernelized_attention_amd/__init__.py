@@ -5,7 +5,8 @@ device memory and streams only.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, FavorError, LIB_PATH, favor_attention, favor_attention_resolve_path,
-    favor_attention_backward, favor_attention_backward_workspace_bytes,
+    favor_attention_backward, favor_attention_backward_resolve_path,
+    favor_attention_backward_workspace_bytes,
     favor_attention_workspace_bytes, favor_embed_bf16, favor_linear_bf16, favor_orf_omega,
     favor_performer_block, favor_profile_attention, lib, loaded_hip_runtimes, status_string,
 )

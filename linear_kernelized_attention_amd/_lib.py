@@ -34,6 +34,7 @@ EXPORTS = (
     "favor_attention", "favor_attention_ex", "favor_attention_resolve_path",
     "favor_profile_attention", "favor_embed_bf16", "favor_linear_bf16",
     "favor_attention_backward_workspace_bytes", "favor_attention_backward",
+    "favor_attention_backward_workspace_bytes_ex", "favor_attention_backward_ex",
 )
 
 
@@ -64,6 +65,8 @@ def _declare(lib: ctypes.CDLL) -> None:
         "favor_linear_bf16": (i, [p, p, p, i, i, i, i, i, i, p]),
         "favor_attention_backward_workspace_bytes": (z, [i] * 8),
         "favor_attention_backward": (i, [p] * 8 + [i] * 8 + [p, z, p]),
+        "favor_attention_backward_workspace_bytes_ex": (z, [i] * 9),
+        "favor_attention_backward_ex": (i, [p] * 8 + [i] * 8 + [p, z, p, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -198,13 +201,13 @@ def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, pa
 
 
 def favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="trig",
-                                             causal=False) -> int:
-    return int(lib().favor_attention_backward_workspace_bytes(
-        B, H, L, d, m, DTYPE[dtype], KIND[kind], int(bool(causal))))
+                                             causal=False, path="auto") -> int:
+    return int(lib().favor_attention_backward_workspace_bytes_ex(
+        B, H, L, d, m, DTYPE[dtype], KIND[kind], int(bool(causal)), PATH[path]))
 
 
 def favor_attention_backward(q, k, v, omega, dout, kind: str = "trig", causal: bool = False,
-                             workspace=None, grads=None):
+                             path: str = "auto", workspace=None, grads=None):
     """(dq, dk, dv) of sum(dout * favor_attention(q, k, v)) on the GPU; grads
     may supply the three output tensors."""
     import torch
@@ -219,17 +222,24 @@ def favor_attention_backward(q, k, v, omega, dout, kind: str = "trig", causal: b
     for t in grads:
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("grads must be contiguous tensors like q")
-    need = int(lib().favor_attention_backward_workspace_bytes(B, H, L, d, m, dt, KIND[kind],
-                                                              int(bool(causal))))
+    need = int(lib().favor_attention_backward_workspace_bytes_ex(B, H, L, d, m, dt, KIND[kind],
+                                                                 int(bool(causal)), PATH[path]))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads
-    _check(lib().favor_attention_backward(
+    _check(lib().favor_attention_backward_ex(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, m, dt, KIND[kind],
-        int(bool(causal)), workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device)),
-        "favor_attention_backward")
+        int(bool(causal)), workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device),
+        PATH[path]), "favor_attention_backward")
     return dq, dk, dv
+
+
+def favor_attention_backward_resolve_path(B, H, L, d, m, dtype="bf16", kind="trig",
+                                          causal=False) -> str:
+    """The kernel family favor_attention_backward runs ("mfma" or "generic")."""
+    ws_m = favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype, kind, causal, "mfma")
+    return "mfma" if ws_m > 0 else "generic"
 
 
 def favor_profile_attention(q, k, v, omega, kind="trig", causal=False, path="auto", iters=20,

@@ -124,12 +124,33 @@ int launch(const Checked& c, const void* Q, const void* K, const void* V, const 
 
 // Backward: the forward checks, plus dOut and the three gradient outputs,
 // which must not overlap any input, each other or the workspace.
+int resolve_backward(const Problem& p, int path) {
+  switch (path) {
+    case FAVOR_PATH_AUTO:
+      if (favor::mfma::supports_backward(p)) return FAVOR_PATH_MFMA;
+      if (favor::generic::supports(p)) return FAVOR_PATH_GENERIC;
+      return FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_GENERIC:
+      return favor::generic::supports(p) ? FAVOR_PATH_GENERIC : FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_MFMA:
+      return favor::mfma::supports_backward(p) ? FAVOR_PATH_MFMA : FAVOR_ERR_UNSUPPORTED;
+    default:
+      return FAVOR_ERR_INVALID_ARG;
+  }
+}
+
+size_t bwd_ws_bytes(const Problem& p, int resolved) {
+  return resolved == FAVOR_PATH_MFMA ? favor::mfma::backward_workspace_bytes(p)
+                                     : favor::generic::backward_workspace_bytes(p);
+}
+
 int check_backward(const void* Q, const void* K, const void* V, const float* Omega,
                    const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L, int d,
                    int m, int dtype, int kind, int causal, void* ws, size_t ws_bytes_given,
-                   Checked* c) {
+                   int path, Checked* c) {
   int st = check_problem(B, H, L, d, m, dtype, kind, causal, &c->p, &c->empty);
   if (st != FAVOR_OK) return st;
+  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
   c->path = FAVOR_PATH_GENERIC;
   if (c->empty) return FAVOR_OK;
   if (!Q || !K || !V || !Omega || !dOut || !dQ || !dK || !dV) return FAVOR_ERR_INVALID_ARG;
@@ -137,8 +158,10 @@ int check_backward(const void* Q, const void* K, const void* V, const float* Ome
   for (const void* x : al)
     if (!aligned16(x)) return FAVOR_ERR_INVALID_ARG;
   if (ws && !aligned16(ws)) return FAVOR_ERR_INVALID_ARG;
-  if (!favor::generic::supports(c->p)) return FAVOR_ERR_UNSUPPORTED;
-  const size_t need = favor::generic::backward_workspace_bytes(c->p);
+  const int r = resolve_backward(c->p, path);
+  if (r < 0) return r;
+  c->path = r;
+  const size_t need = bwd_ws_bytes(c->p, r);
   if (need > 0 && (!ws || ws_bytes_given < need)) return FAVOR_ERR_WORKSPACE;
   const size_t esz = dtype == FAVOR_DTYPE_F32 ? 4 : 2;
   const size_t tensor = (size_t)c->p.BH * (size_t)L * (size_t)d * esz;
@@ -323,32 +346,49 @@ int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K
   return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
-size_t favor_attention_backward_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
-                                                int kind, int causal) {
+size_t favor_attention_backward_workspace_bytes_ex(int B, int H, int L, int d, int m, int dtype,
+                                                   int kind, int causal, int path) {
   Problem p;
   bool empty;
   if (check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty) != FAVOR_OK) return 0;
-  if (empty || !favor::generic::supports(p)) return 0;
-  return favor::generic::backward_workspace_bytes(p);
+  if (empty) return 0;
+  const int r = resolve_backward(p, path);
+  return r < 0 ? 0 : bwd_ws_bytes(p, r);
+}
+
+size_t favor_attention_backward_workspace_bytes(int B, int H, int L, int d, int m, int dtype,
+                                                int kind, int causal) {
+  return favor_attention_backward_workspace_bytes_ex(B, H, L, d, m, dtype, kind, causal,
+                                                     FAVOR_PATH_AUTO);
+}
+
+int favor_attention_backward_ex(const void* Q, const void* K, const void* V, const float* Omega,
+                                const void* dOut, void* dQ, void* dK, void* dV, int B, int H,
+                                int L, int d, int m, int dtype, int kind, int causal,
+                                void* workspace, size_t workspace_bytes, void* stream, int path) {
+  Checked c;
+  int st = check_backward(Q, K, V, Omega, dOut, dQ, dK, dV, B, H, L, d, m, dtype, kind, causal,
+                          workspace, workspace_bytes, path, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  favor::Buffers b{Q, K, V, Omega, nullptr, workspace, workspace_bytes};
+  favor::BwdBuffers g{dOut, dQ, dK, dV};
+  const hipError_t e = c.path == FAVOR_PATH_MFMA
+                           ? favor::mfma::run_backward(c.p, b, g, (hipStream_t)stream, nullptr)
+                           : favor::generic::run_backward(c.p, b, g, (hipStream_t)stream, nullptr);
+  if (e != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipPeekAtLastError() != hipSuccess) {
+    (void)hipGetLastError();
+    return FAVOR_ERR_HIP;
+  }
+  return FAVOR_OK;
 }
 
 int favor_attention_backward(const void* Q, const void* K, const void* V, const float* Omega,
                              const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L,
                              int d, int m, int dtype, int kind, int causal, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  Checked c;
-  int st = check_backward(Q, K, V, Omega, dOut, dQ, dK, dV, B, H, L, d, m, dtype, kind, causal,
-                          workspace, workspace_bytes, &c);
-  if (st != FAVOR_OK || c.empty) return st;
-  favor::Buffers b{Q, K, V, Omega, nullptr, workspace, workspace_bytes};
-  favor::BwdBuffers g{dOut, dQ, dK, dV};
-  if (favor::generic::run_backward(c.p, b, g, (hipStream_t)stream, nullptr) != hipSuccess)
-    return FAVOR_ERR_HIP;
-  if (hipPeekAtLastError() != hipSuccess) {
-    (void)hipGetLastError();
-    return FAVOR_ERR_HIP;
-  }
-  return FAVOR_OK;
+  return favor_attention_backward_ex(Q, K, V, Omega, dOut, dQ, dK, dV, B, H, L, d, m, dtype, kind,
+                                     causal, workspace, workspace_bytes, stream, FAVOR_PATH_AUTO);
 }
 
 }  // extern "C"

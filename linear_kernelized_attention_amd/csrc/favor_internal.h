@@ -84,6 +84,16 @@ namespace mfma {
 bool supports(const Problem& p);
 size_t workspace_bytes(const Problem& p);
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+// backward pass (bidirectional)
+bool supports_backward(const Problem& p);
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
+                        PhaseHook* hook);
+size_t dphi_lds(const Problem& p);
+hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
+                       const float* Omega, const uint16_t* part, long long stride, int nsum,
+                       const uint16_t* Wv, const float* wz, uint16_t* DX, bool keys,
+                       hipStream_t s);
 }  // namespace mfma
 
 namespace block {

@@ -149,13 +149,16 @@ constexpr int KV_NBUF = 3;
 constexpr size_t KV_LDS_BYTES =
     (size_t)KV_NBUF * ((TK * KROW + NCOL * VROW) * sizeof(uint16_t) + TK * sizeof(float));
 
-template <int KIND, int NW>
+//
+// ZSRC (backward pass): the rows are [a_t, b_t] with no key weight -- V
+// holds a_t and column 64 takes b_t from zsrc [BH][L] instead of c_t.
+template <int KIND, int NW, bool ZSRC = false>
 __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                       const float* __restrict__ Omega, uint16_t* __restrict__ part,
                                       uint16_t* __restrict__ ofrag, int L, int M, int n_fpart,
                                       int seg_len, long long BH,
                                       float omega_scale, float knorm_scale, long long bh, int task,
-                                      uint16_t* lds) {
+                                      uint16_t* lds, const float* __restrict__ zsrc = nullptr) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr bool POS = KIND == KIND_POS;
   constexpr int FT = TRIG ? 2 : 1;      // feature tiles per wave (sin, cos)
@@ -231,7 +234,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       const int task = tid + k * NT;
       const int q = (task >> 3) & (TK / 2 - 1), c8 = task & 7;
       const int t = pair_token(q);
-      float ct[2];
+      float ct[2], zv[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint16_t* kv = (const uint16_t*)&raw.k[k][h];
@@ -245,7 +248,9 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
         // 2^(log2(e) |k~|^2 / 2): c_t of the trig map, and (positive map)
         // the exponent offset that stays in the feature
         const float e2 = ss * half_log2e_knorm;
-        ct[h] = (t0 + t + h < seg1) ? (TRIG ? __builtin_amdgcn_exp2f(e2) : 1.f) : 0.f;
+        const bool valid = t0 + t + h < seg1;
+        ct[h] = valid ? (TRIG && !ZSRC ? __builtin_amdgcn_exp2f(e2) : 1.f) : 0.f;
+        zv[h] = ZSRC ? (valid ? zsrc[(size_t)bh * L + t0 + t + h] : 0.f) : ct[h];
         if (POS && c8 == 0 && task < NTASK) Hn[buf][t + h] = e2;
       }
       if (CH * NT != NTASK && task >= NTASK) continue;
@@ -260,7 +265,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       // value column D holds c_t (the z column); the lanes of the other
       // chunks write the same word into padding columns that are never read
       // back into a stored result
-      *(uint32_t*)&Vt[buf][vt_index(D + c8, 2 * q)] = pack2(ct[0], ct[1]);
+      *(uint32_t*)&Vt[buf][vt_index(D + c8, 2 * q)] = pack2(zv[0], zv[1]);
     }
   };
 
@@ -416,7 +421,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
 
 // Standalone key-side kernel: one task per block, blocks numbered so that
 // the tasks of a head run on one XCD.
-template <int KIND, int NW>
+template <int KIND, int NW, bool ZSRC = false>
 __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
                                                            const float* __restrict__ Omega,
@@ -424,12 +429,13 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ ofrag, int L,
                                                            int M, int n_fpart, int seg_len,
                                                            long long BH, float omega_scale,
-                                                           float knorm_scale) {
+                                                           float knorm_scale,
+                                                           const float* __restrict__ zsrc) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[KV_LDS_BYTES / sizeof(uint16_t)];
   const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
   const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  kv_state_block<KIND, NW>(K, V, Omega, part, ofrag, L, M, n_fpart, seg_len, BH, omega_scale,
-                           knorm_scale, lb / nx, (int)(lb % nx), lds);
+  kv_state_block<KIND, NW, ZSRC>(K, V, Omega, part, ofrag, L, M, n_fpart, seg_len, BH, omega_scale,
+                                 knorm_scale, lb / nx, (int)(lb % nx), lds, zsrc);
 }
 
 // ------------------------------------------------------- key-side host
@@ -478,27 +484,27 @@ inline dim3 head_grid(long long x, long long BH) {
   return dim3((unsigned)x, (unsigned)y, (unsigned)z);
 }
 
-template <int KIND, int NW>
+template <int KIND, int NW, bool ZSRC = false>
 inline void launch_kv(const Problem& p, const Buffers& b, const Plan& pl, uint16_t* ofrag,
-                      hipStream_t s, float oscale) {
-  hipLaunchKernelGGL((kv_state_kernel<KIND, NW>), dim3((unsigned)((long long)pl.n_split * pl.n_fpart * p.BH)),
+                      hipStream_t s, float oscale, const float* zsrc = nullptr) {
+  hipLaunchKernelGGL((kv_state_kernel<KIND, NW, ZSRC>), dim3((unsigned)((long long)pl.n_split * pl.n_fpart * p.BH)),
                      dim3(NW * 64), 0, s, (const uint16_t*)b.k, (const uint16_t*)b.v, b.omega,
                      (uint16_t*)b.ws, ofrag, p.L, p.m, pl.n_fpart, pl.seg_len, p.BH, oscale,
-                     1.0f / sqrtf((float)D));
+                     1.0f / sqrtf((float)D), zsrc);
 }
 
-template <int KIND>
+template <int KIND, bool ZSRC = false>
 inline void launch_kv_nw(const Problem& p, const Buffers& b, const Plan& pl, uint16_t* ofrag,
-                         hipStream_t s, float oscale) {
+                         hipStream_t s, float oscale, const float* zsrc = nullptr) {
   switch (pl.nw_kv) {
-    case 1: launch_kv<KIND, 1>(p, b, pl, ofrag, s, oscale); break;
-    case 2: launch_kv<KIND, 2>(p, b, pl, ofrag, s, oscale); break;
-    case 3: launch_kv<KIND, 3>(p, b, pl, ofrag, s, oscale); break;
-    case 4: launch_kv<KIND, 4>(p, b, pl, ofrag, s, oscale); break;
-    case 5: launch_kv<KIND, 5>(p, b, pl, ofrag, s, oscale); break;
-    case 6: launch_kv<KIND, 6>(p, b, pl, ofrag, s, oscale); break;
-    case 7: launch_kv<KIND, 7>(p, b, pl, ofrag, s, oscale); break;
-    default: launch_kv<KIND, 8>(p, b, pl, ofrag, s, oscale); break;
+    case 1: launch_kv<KIND, 1, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 2: launch_kv<KIND, 2, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 3: launch_kv<KIND, 3, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 4: launch_kv<KIND, 4, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 5: launch_kv<KIND, 5, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 6: launch_kv<KIND, 6, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    case 7: launch_kv<KIND, 7, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
+    default: launch_kv<KIND, 8, ZSRC>(p, b, pl, ofrag, s, oscale, zsrc); break;
   }
 }
 

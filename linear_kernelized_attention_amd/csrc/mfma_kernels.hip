@@ -91,11 +91,20 @@ constexpr size_t readout_lds_bytes() {
   return ((size_t)(F / 32) * 5 + (size_t)(M / 16) * 2) * 512 * sizeof(uint16_t);
 }
 
-template <int KIND, int NW, int NPAIR>
+// MODE selects the epilogue: RO_OUT writes out = num / den (the forward);
+// the backward pass uses RO_AB, which reads dOut = G and writes
+// a = G / den (to out) and b = -(G . num) / den^2 (to bhat [BH][L],
+// float32), and RO_DV, which writes num scaled by the token's key weight
+// c = exp(|x~|^2 / 2) for the trig map (1 otherwise), with no division.
+enum { RO_OUT = 0, RO_AB = 1, RO_DV = 2 };
+
+template <int KIND, int NW, int NPAIR, int MODE = RO_OUT>
 __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ ofrag,
                                      const uint16_t* __restrict__ part, long long split_stride,
                                      int nsum, uint16_t* __restrict__ out, int L, long long bh,
-                                     int qblock, uint16_t* smem) {
+                                     int qblock, uint16_t* smem,
+                                     const uint16_t* __restrict__ G = nullptr,
+                                     float* __restrict__ bhat = nullptr) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr bool POS = KIND == KIND_POS;
   constexpr int M = 32 * NPAIR;
@@ -125,7 +134,7 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
   // positive map: the exponent offset log2(e) |q~|^2 / 2 of token
   // t0 + 16 nt + c (the four lane groups each hold 16 of its 64 values)
   float hq[4] = {0.f, 0.f, 0.f, 0.f};
-  if (POS) {
+  if (POS || (TRIG && MODE == RO_DV)) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float ss = 0.f;
@@ -138,7 +147,9 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         }
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
-      hq[nt] = 0.5f * LOG2E * ss * (1.0f / 8.0f);   // |q~|^2 = |q|^2 / sqrt(64)
+      // log2(e) |q~|^2 / 2 with |q~|^2 = |q|^2 / sqrt(64): the positive map's
+      // exponent offset, and (RO_DV, trig) log2 of the key weight
+      hq[nt] = 0.5f * LOG2E * ss * (1.0f / 8.0f);
     }
   }
   // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
@@ -334,12 +345,35 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
   uint16_t* ob = smem + (size_t)w * QW * OROW;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const float inv = 1.0f / acc[4][nt][0];
+    float mul = 1.0f / acc[4][nt][0];
+    if (MODE == RO_DV) mul = TRIG ? __builtin_amdgcn_exp2f(hq[nt]) : 1.0f;
+    if (MODE == RO_AB) {
+      // b = -(g . num) / den^2: this lane's 16 columns, then the 4 lane groups
+      const long long tok = min(t0 + 16 * nt + c, (long long)L - 1);
+      float gv[4][4], gn = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x2 raw = *(const u32x2*)(G + head + (size_t)tok * D + 16 * mt + 4 * g);
+        gv[mt][0] = __uint_as_float(raw[0] << 16);
+        gv[mt][1] = __uint_as_float(raw[0] & 0xffff0000u);
+        gv[mt][2] = __uint_as_float(raw[1] << 16);
+        gv[mt][3] = __uint_as_float(raw[1] & 0xffff0000u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gn = fmaf(gv[mt][r], acc[mt][nt][r], gn);
+      }
+      gn += __shfl_xor(gn, 16);
+      gn += __shfl_xor(gn, 32);
+      if (g == 0 && t0 + 16 * nt + c < L) bhat[(size_t)bh * L + t0 + 16 * nt + c] = -gn * mul * mul;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = gv[mt][r];
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       u32x2 o;
-      o[0] = pack2(acc[mt][nt][0] * inv, acc[mt][nt][1] * inv);
-      o[1] = pack2(acc[mt][nt][2] * inv, acc[mt][nt][3] * inv);
+      o[0] = pack2(acc[mt][nt][0] * mul, acc[mt][nt][1] * mul);
+      o[1] = pack2(acc[mt][nt][2] * mul, acc[mt][nt][3] * mul);
       *(u32x2*)(ob + (16 * nt + c) * OROW + 16 * mt + 4 * g) = o;
     }
   }
@@ -356,18 +390,20 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
 }
 
 // Standalone query-side kernel: one task per block.
-template <int KIND, int NW, int NPAIR>
+template <int KIND, int NW, int NPAIR, int MODE = RO_OUT>
 __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ ofrag,
                                                           const uint16_t* __restrict__ part,
                                                           long long split_stride, int nsum,
                                                           uint16_t* __restrict__ out, int L,
-                                                          long long BH) {
+                                                          long long BH,
+                                                          const uint16_t* __restrict__ G,
+                                                          float* __restrict__ bhat) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
   const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  readout_block<KIND, NW, NPAIR>(Q, ofrag, part, split_stride, nsum, out, L, lb / nx, (int)(lb % nx),
-                                 smem);
+  readout_block<KIND, NW, NPAIR, MODE>(Q, ofrag, part, split_stride, nsum, out, L, lb / nx,
+                                       (int)(lb % nx), smem, G, bhat);
 }
 
 // ---------------------------------------------------------------- host
@@ -389,29 +425,31 @@ void allow_full_lds(Kern kern) {
   (void)done;
 }
 
-template <int KIND, int NPAIR>
+template <int KIND, int NPAIR, int MODE>
 void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
-                    int nsum, const uint16_t* ofrag, hipStream_t s) {
-  auto kern = readout_kernel<KIND, RO_NW, NPAIR>;
+                    int nsum, const uint16_t* ofrag, hipStream_t s, const uint16_t* G,
+                    float* bhat) {
+  auto kern = readout_kernel<KIND, RO_NW, NPAIR, MODE>;
   allow_full_lds(kern);
   const long long nb = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(RO_NW * 64), readout_lds(p), s,
                      (const uint16_t*)b.q, ofrag, part, split_stride, nsum, (uint16_t*)b.out, p.L,
-                     p.BH);
+                     p.BH, G, bhat);
 }
 
-template <int KIND>
+template <int KIND, int MODE = RO_OUT>
 void launch_readout_m(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
-                      int nsum, const uint16_t* ofrag, hipStream_t s) {
+                      int nsum, const uint16_t* ofrag, hipStream_t s, const uint16_t* G = nullptr,
+                      float* bhat = nullptr) {
   switch (p.m / 32) {
-    case 1: launch_readout<KIND, 1>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 2: launch_readout<KIND, 2>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 3: launch_readout<KIND, 3>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 4: launch_readout<KIND, 4>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 5: launch_readout<KIND, 5>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 6: launch_readout<KIND, 6>(p, b, part, split_stride, nsum, ofrag, s); break;
-    case 7: launch_readout<KIND, 7>(p, b, part, split_stride, nsum, ofrag, s); break;
-    default: launch_readout<KIND, 8>(p, b, part, split_stride, nsum, ofrag, s); break;
+    case 1: launch_readout<KIND, 1, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 2: launch_readout<KIND, 2, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 3: launch_readout<KIND, 3, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 4: launch_readout<KIND, 4, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 5: launch_readout<KIND, 5, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 6: launch_readout<KIND, 6, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 7: launch_readout<KIND, 7, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    default: launch_readout<KIND, 8, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
   }
 }
 
@@ -457,6 +495,97 @@ hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook
 
 bool lds_fits(const Problem& p) { return readout_lds(p) <= 160 * 1024; }
 
+// ------------------------------------------------------------- backward
+// Workspace: S partials, the summed S (beyond RO_MAXSUM splits), Omega~
+// fragments, a (bf16 [BH][L][64]), b (float32 [BH][L]), R partials and the
+// summed R.
+struct BwdLayout {
+  Plan pl;
+  size_t red, ab, bh, total;
+};
+
+BwdLayout bwd_layout(const Problem& p) {
+  BwdLayout bl;
+  bl.pl = plan_keys(p, 256, TK);
+  bl.red = red_bytes(p, bl.pl);
+  bl.ab = align_up((size_t)p.BH * p.L * D * sizeof(uint16_t), 256);
+  bl.bh = align_up((size_t)p.BH * p.L * sizeof(float), 256);
+  bl.total = 2 * (bl.pl.part_bytes + bl.red) + bl.pl.ofrag_bytes + bl.ab + bl.bh;
+  return bl;
+}
+
+template <int KIND>
+hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffers& gb, hipStream_t s,
+                             PhaseHook* hook) {
+  const float oscale = omega_scale_for(KIND);
+  const BwdLayout bl = bwd_layout(p);
+  const Plan& pl = bl.pl;
+  char* ws = (char*)b.ws;
+  uint16_t* partS = (uint16_t*)ws;
+  uint16_t* redS = (uint16_t*)(ws + pl.part_bytes);
+  uint16_t* ofrag = (uint16_t*)(ws + pl.part_bytes + bl.red);
+  uint16_t* ab = (uint16_t*)((char*)ofrag + pl.ofrag_bytes);
+  float* bhat = (float*)((char*)ab + bl.ab);
+  uint16_t* partR = (uint16_t*)((char*)bhat + bl.bh);
+  uint16_t* redR = (uint16_t*)((char*)partR + pl.part_bytes);
+  const long long stride = (long long)split_stride_elems(p);
+  const long long per8 = stride / 8;
+  auto sum_splits = [&](const uint16_t* part, uint16_t* red, const uint16_t** src, int* nsum) {
+    *src = part;
+    *nsum = pl.n_split;
+    if (pl.n_split > RO_MAXSUM) {
+      hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((per8 + 255) / 256)), dim3(256), 0, s,
+                         part, red, pl.n_split, per8);
+      *src = red;
+      *nsum = 1;
+    }
+  };
+  const uint16_t* srcS;
+  const uint16_t* srcR;
+  int nS, nR;
+
+  // forward state S from (K, V)
+  phase_begin(hook, s, "mfma_kv_state");
+  Buffers bk = b;
+  bk.ws = partS;
+  launch_kv_nw<KIND>(p, bk, pl, ofrag, s, oscale);
+  sum_splits(partS, redS, &srcS, &nS);
+  phase_end(hook, s);
+  // a = g / den, b = -(g . num) / den^2 per query
+  phase_begin(hook, s, "mfma_bwd_ab");
+  Buffers bq = b;
+  bq.out = ab;
+  launch_readout_m<KIND, RO_AB>(p, bq, srcS, stride, nS, ofrag, s, (const uint16_t*)gb.dout, bhat);
+  phase_end(hook, s);
+  // R = sum_i u(q_i) [a_i, b_i]^T: the key-side kernel on (Q, a) with b in column 64
+  phase_begin(hook, s, "mfma_bwd_rstate");
+  Buffers br = b;
+  br.k = b.q;
+  br.v = ab;
+  br.ws = partR;
+  launch_kv_nw<KIND, true>(p, br, pl, nullptr, s, oscale, bhat);
+  sum_splits(partR, redR, &srcR, &nR);
+  phase_end(hook, s);
+  // dQ from (S, [a, b]); dK from (R, [v, 1]); dV = R^T u(k) (trig: times c_k)
+  phase_begin(hook, s, "mfma_bwd_dq");
+  hipError_t e = launch_dphi(p, (const uint16_t*)b.q, ofrag, b.omega, srcS, stride, nS, ab, bhat,
+                             (uint16_t*)gb.dq, false, s);
+  phase_end(hook, s);
+  if (e != hipSuccess) return e;
+  phase_begin(hook, s, "mfma_bwd_dk");
+  e = launch_dphi(p, (const uint16_t*)b.k, ofrag, b.omega, srcR, stride, nR, (const uint16_t*)b.v,
+                  nullptr, (uint16_t*)gb.dk, true, s);
+  phase_end(hook, s);
+  if (e != hipSuccess) return e;
+  phase_begin(hook, s, "mfma_bwd_dv");
+  Buffers bv = b;
+  bv.q = b.k;
+  bv.out = gb.dv;
+  launch_readout_m<KIND, RO_DV>(p, bv, srcR, stride, nR, ofrag, s);
+  phase_end(hook, s);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t causal_workspace_bytes(const Problem& p);
@@ -471,6 +600,19 @@ size_t workspace_bytes(const Problem& p) {
   if (p.causal) return causal_workspace_bytes(p);
   const Plan pl = plan_keys(p, 256, TK);
   return pl.part_bytes + red_bytes(p, pl) + pl.ofrag_bytes;
+}
+
+bool supports_backward(const Problem& p) {
+  return !p.causal && supports(p) && dphi_lds(p) <= 160 * 1024;
+}
+
+size_t backward_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
+
+hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
+                        PhaseHook* hook) {
+  if (p.kind == KIND_TRIG) return run_backward_kind<KIND_TRIG>(p, b, g, s, hook);
+  if (p.kind == KIND_POS) return run_backward_kind<KIND_POS>(p, b, g, s, hook);
+  return run_backward_kind<KIND_RELU>(p, b, g, s, hook);
 }
 
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook) {

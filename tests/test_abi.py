@@ -177,7 +177,14 @@ def test_backward_alias_checks():
 
 
 def test_backward_workspace_covers_forward_state():
+    shape = (1, 8, 4096, 64, 256, "bf16", "trig")
     for causal in (False, True):
-        fwd = F.favor_attention_workspace_bytes(1, 8, 4096, 64, 256, "bf16", "trig", causal, "generic")
-        bwd = F.favor_attention_backward_workspace_bytes(1, 8, 4096, 64, 256, "bf16", "trig", causal)
+        fwd = F.favor_attention_workspace_bytes(*shape, causal, "generic")
+        bwd = F.favor_attention_backward_workspace_bytes(*shape, causal, "generic")
         assert bwd > fwd
+    assert (F.favor_attention_backward_workspace_bytes(*shape, False, "mfma")
+            > F.favor_attention_workspace_bytes(*shape, False, "mfma"))
+    # the MFMA backward is bidirectional only
+    assert F.favor_attention_backward_workspace_bytes(*shape, True, "mfma") == 0
+    assert F.favor_attention_backward_resolve_path(1, 8, 4096, 64, 256, "bf16", "trig", True) == "generic"
+    assert F.favor_attention_backward_resolve_path(1, 8, 4096, 64, 256, "bf16", "trig", False) == "mfma"

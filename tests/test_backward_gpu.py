@@ -54,17 +54,26 @@ def _grad_err(got, ref, scale_ref):
     return float(max(errs))
 
 
-def _check(shape, kind, causal, seed=0, workers=None):
+def _paths(shape, kind, causal):
+    B, H, L, d, m, dtype = shape
+    paths = ["generic"]
+    if F.favor_attention_backward_resolve_path(B, H, L, d, m, dtype, kind, causal) == "mfma":
+        paths.append("mfma")
+    return paths
+
+
+def _check(shape, kind, causal, seed=0, workers=None, paths=None):
     dtype = shape[-1]
     dev, (q, k, v), W, g_dev, g64 = _grad_problem(shape, kind, causal, seed)
     ref = O.favor_attention_grad(q, k, v, W, g64, kind, causal, workers=workers)
-    got = F.favor_attention_backward(*dev, g_dev, kind=kind, causal=causal)
-    torch.cuda.synchronize()
-    errs = [_grad_err(from_device(x), r, ref[2]) for x, r in zip(got, ref)]
-    print(f"{shape} {kind} causal={causal} dq/dk/dv rel = " + " ".join(f"{e:.2e}" for e in errs),
-          flush=True)
-    for name, e in zip(("dq", "dk", "dv"), errs):
-        assert e <= TOL[dtype], (name, e)
+    for path in paths or _paths(shape, kind, causal):
+        got = F.favor_attention_backward(*dev, g_dev, kind=kind, causal=causal, path=path)
+        torch.cuda.synchronize()
+        errs = [_grad_err(from_device(x), r, ref[2]) for x, r in zip(got, ref)]
+        print(f"[{path}] {shape} {kind} causal={causal} dq/dk/dv rel = "
+              + " ".join(f"{e:.2e}" for e in errs), flush=True)
+        for name, e in zip(("dq", "dk", "dv"), errs):
+            assert e <= TOL[dtype], (path, name, e)
 
 
 @pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
@@ -80,27 +89,41 @@ def test_backward_config2_shape(causal):
     _check((8, 8, 1024, 64, 256, "bf16"), "trig", causal, workers=O.default_workers())
 
 
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
+def test_backward_mfma_headline_shape(kind):
+    # B4 H8 L4096 d64 m256 bf16 bidirectional (4 token splits per head)
+    _check((4, 8, 4096, 64, 256, "bf16"), kind, False, workers=O.default_workers(), paths=["mfma"])
+
+
+def test_backward_mfma_many_splits():
+    # L = 32768 with 8 heads: more splits than the readout sums itself
+    _check((1, 8, 32768, 64, 256, "bf16"), "trig", False, workers=O.default_workers(), paths=["mfma"])
+
+
 def test_backward_config1():
     _check((1, 1, 512, 16, 64, "f32"), "trig", False)
 
 
-def test_backward_workspace_contents_ignored():
+@pytest.mark.parametrize("causal,path", [(True, "generic"), (False, "mfma")])
+def test_backward_workspace_contents_ignored(causal, path):
     shape = (1, 2, 300, 64, 256, "bf16")
-    dev, (q, k, v), W, g_dev, g64 = _grad_problem(shape, "trig", True, 3)
-    ref = O.favor_attention_grad(q, k, v, W, g64, "trig", True)
-    need = F.favor_attention_backward_workspace_bytes(1, 2, 300, 64, 256, "bf16", "trig", True)
+    dev, (q, k, v), W, g_dev, g64 = _grad_problem(shape, "trig", causal, 3)
+    ref = O.favor_attention_grad(q, k, v, W, g64, "trig", causal)
+    need = F.favor_attention_backward_workspace_bytes(1, 2, 300, 64, 256, "bf16", "trig", causal, path)
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
-    got = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=True, workspace=ws)
+    got = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=causal, workspace=ws,
+                                     path=path)
     torch.cuda.synchronize()
     for x, r in zip(got, ref):
         assert slice_rel_err(from_device(x), r) <= 2e-2
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_deterministic(causal):
     shape = (2, 2, 600, 64, 128, "bf16")
-    dev, _, _, g_dev, _ = _grad_problem(shape, "trig", True, 4)
-    a = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=True)
-    b = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=True)
+    dev, _, _, g_dev, _ = _grad_problem(shape, "trig", causal, 4)
+    a = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=causal)
+    b = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=causal)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
