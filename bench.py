@@ -104,12 +104,15 @@ def load_traffic(kernel: str):
     return float(ent["bytes_per_launch"])
 
 
-def upload(ai, dtype):
+def upload_one(x, dtype):
     import torch
     if dtype == "f32":
-        return [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (ai.q, ai.k, ai.v)]
-    return [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
-            for x in (ai.q, ai.k, ai.v)]
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def upload(ai, dtype):
+    return [upload_one(x, dtype) for x in (ai.q, ai.k, ai.v)]
 
 
 def time_calls(fn, steps, warmup):
@@ -152,6 +155,33 @@ def bench_block(F, I, steps, warmup):
     ids = torch.from_numpy(b.ids).cuda()
     fn = lambda: F.favor_performer_block(ids, *dev, omega, heads=cfg["H"], kind=cfg["kind"])
     return time_calls(fn, steps, warmup)
+
+
+def bench_backward(F, I, w, steps, warmup):
+    """Seconds per favor_attention_backward call on a workload's seeded
+    inputs and a seeded N(0, 1) output gradient."""
+    import torch
+    ai, dr = I.workload_inputs(w)
+    q, k, v = upload(ai, w.dtype)
+    gs, _ = I.output_grads(w.B, w.H, w.L, w.d, w.dtype)
+    g = upload_one(gs, w.dtype)
+    omega = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, w.m)).cuda()
+    need = F.favor_attention_backward_workspace_bytes(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind,
+                                                      w.causal)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    fn = lambda: F.favor_attention_backward(q, k, v, omega, g, kind=w.kind, causal=w.causal,
+                                            workspace=ws, grads=grads)
+    return time_calls(fn, steps, warmup)
+
+
+def backward_work(B, H, L, d, m, kind):
+    """Algorithmic flops of one backward call that recomputes the forward
+    state: phi projections of q and k (4dm), S/z and num/den (4F(d+1)),
+    dphi(q), R, dV and dphi(k) (8F(d+1)) and the projections' adjoints
+    (4dm) per token-head."""
+    F_ = feature_width(m, kind)
+    return B * H * L * (8 * d * m + 12 * F_ * (d + 1))
 
 
 def bench_random(F, shape, kind, causal, steps, warmup):
@@ -327,6 +357,18 @@ def main():
                           steps, 3)
         extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": cfg["B"] * cfg["L"] / sb,
                              "favor_us_per_call": sf * 1e6}
+        # backward pass on the headline, causal and B8 H8 L1024 shapes
+        for key in ("head", "c3_causal", "c2_trig"):
+            wk = I.WORKLOADS[key]
+            sbw = bench_backward(F, I, wk, max(5, steps // 10), 2)
+            fl = backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind)
+            rp = F.favor_attention_backward_resolve_path(wk.B, wk.H, wk.L, wk.d, wk.m, wk.dtype,
+                                                         wk.kind, wk.causal)
+            peak = PEAK_BF16_MFMA_TFLOPS if rp == "mfma" else PEAK_FP32_VALU_TFLOPS
+            extra[f"bwd_{key}"] = {"us_per_call": sbw * 1e6, "tokens_x_heads_per_s": wk.tokens_x_heads / sbw,
+                                   "path": rp, "algorithmic_tflops": fl / sbw / 1e12,
+                                   "peak_frac": fl / sbw / 1e12 / peak,
+                                   "peak": "bf16 MFMA" if rp == "mfma" else "fp32 VALU"}
         # saturation: the headline shape at larger batch (timing on random inputs)
         sweep = {}
         for Bs in (8, 16, 32):
