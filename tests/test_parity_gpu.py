@@ -40,6 +40,9 @@ SMALL = [
     (1, 3, 257, 64, 256, "bf16"),
     (1, 1, 1000, 64, 128, "bf16"),
     (2, 1, 130, 16, 64, "bf16"),
+    # MFMA with Omega rows not a multiple of 128 (6 and 5 waves per key block)
+    (1, 2, 200, 64, 96, "bf16"),
+    (1, 1, 150, 64, 160, "bf16"),
 ]
 
 
