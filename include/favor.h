@@ -180,10 +180,12 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
  *   favor_attention_backward_workspace_bytes(...) bytes, contents
  *   ignored and overwritten; float32 state, [a, b] and suffix buffers.
  * Every pointer is 16-byte aligned device memory owned by the caller.
- * Kernel families: MFMA (bf16, d = 64, m a multiple of 32 up to 256,
- * bidirectional; the forward's kernels plus a fused feature-gradient
- * kernel) and generic (float32 arithmetic; d <= 64, m <= 1024, any L, both
- * directions).  favor_attention_backward picks MFMA when it applies; the
+ * Kernel families: MFMA (bf16, d = 64, m a multiple of 32 up to 256, both
+ * directions; bidirectional: the forward's kernels plus a fused
+ * feature-gradient kernel; causal: the forward's chunk kernel, which also
+ * forms [a, b] and dV, and a chunked feature-gradient kernel that walks
+ * prefix states for dQ and suffix states for dK) and generic (float32
+ * arithmetic; d <= 64, m <= 1024, any L, both directions).  favor_attention_backward picks MFMA when it applies; the
  * _ex variants take a favor_path as for the forward (FAVOR_ERR_UNSUPPORTED
  * if the requested family cannot run the problem).  All checks run before
  * anything is enqueued; execution is asynchronous on `stream`.

@@ -84,7 +84,7 @@ namespace mfma {
 bool supports(const Problem& p);
 size_t workspace_bytes(const Problem& p);
 hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
-// backward pass (bidirectional)
+// backward pass (bidirectional and causal)
 bool supports_backward(const Problem& p);
 size_t backward_workspace_bytes(const Problem& p);
 hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,

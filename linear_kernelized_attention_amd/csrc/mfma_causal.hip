@@ -40,17 +40,19 @@ __device__ inline int ct_index(int row, int s) {
 }
 
 // ------------------------------------------------------------------ scan
-// start[seg] = sum_{s < seg} part[s] elementwise over the per-segment
+// start[seg] = sum_{s < seg} part[s] (rev: sum_{s > seg} part[s], the
+// suffix a reversed walk starts from) elementwise over the per-segment
 // states (any layout): float32 running sums in a fixed order, stored in
 // bf16 (the chunk kernel feeds the start state to bf16 MFMA operands, and
 // continues the sum in float32); one thread per 8 elements.
 __global__ __launch_bounds__(256) void scan_kernel(const uint16_t* __restrict__ part,
                                                    uint16_t* __restrict__ start, int n_seg,
-                                                   long long per_seg8) {
+                                                   long long per_seg8, int rev) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= per_seg8) return;
   float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sg = 0; sg < n_seg; ++sg) {
+  for (int k = 0; k < n_seg; ++k) {
+    const int sg = rev ? n_seg - 1 - k : k;
     const u32x4 v = *(const u32x4*)(part + ((size_t)sg * per_seg8 + i) * 8);
     *(bf16x8*)(start + ((size_t)sg * per_seg8 + i) * 8) = pack8(run);
     const uint16_t* h = (const uint16_t*)&v;
@@ -60,14 +62,29 @@ __global__ __launch_bounds__(256) void scan_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- causal
-template <int KIND, int NW>
+// Modes of the chunk kernel.  C_OUT: the attention output.  The backward
+// pass adds C_AB, which reads dOut = G and writes a = G / den (to out) and
+// b = -(G . num) / den^2 (to bhat [BH][L], float32), and C_DV, the
+// anti-causal numerator sum_{j >= i} (u(q_i) . u(k_j)) v_j -- called with
+// the roles of queries and keys exchanged it yields dV: its "values" carry
+// no key weight, chunks are walked from the last, the start state is the
+// suffix over later segments, and the result is scaled by the query row's
+// trig weight exp(|x~|^2 / 2) instead of normalised.
+enum { C_OUT = 0, C_AB = 1, C_DV = 2 };
+
+template <int KIND, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void causal_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ Omega,
     const uint16_t* __restrict__ start, uint16_t* __restrict__ out, int L, int seg_len, int n_seg,
-    long long BH, float omega_scale, float knorm_scale) {
+    long long BH, float omega_scale, float knorm_scale, const uint16_t* __restrict__ G,
+    float* __restrict__ bhat) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr bool POS = KIND == KIND_POS;
+  constexpr bool REV = MODE == C_DV;
+  // query-row exponent offsets: the positive map's, and log2 of the trig
+  // weight that scales dV
+  constexpr bool QOFF = POS || (TRIG && MODE == C_DV);
   constexpr int M = NW * 32;
   constexpr int F = TRIG ? 2 * M : M;
   constexpr int FT = TRIG ? 4 : 2;    // feature tiles of 16 per wave
@@ -94,6 +111,10 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   // and queries
   __shared__ __attribute__((aligned(16))) float Hk[2][CT];
   __shared__ __attribute__((aligned(16))) float Hq[2][CT];
+  // C_AB: per column tile, the partial dot products G . num of the chunk's
+  // tokens, and the tokens' 1 / den
+  __shared__ float Gp[MODE == C_AB ? 4 : 1][CT];
+  __shared__ float Inv[MODE == C_AB ? CT : 1];
   // per wave: the transposed phi(K) tile, later reused for the partial out^T
   __shared__ __attribute__((aligned(16))) float Red[NW][RED_FLOATS];
   // per wave: its Omega~ fragments (2 row tiles x 2 column halves)
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // squared norms: of the keys, and (positive map) of the query chunk
-        const bool use = kvtask || (POS && h == 0 && task < NQT);
+        const bool use = kvtask || (QOFF && h == 0 && task < NQT);
         const uint16_t* kv = (const uint16_t*)&r.d[k][h];
         float ss = 0.f;
 #pragma unroll
@@ -179,12 +200,12 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
           ss = fmaf(x, x, ss);
         }
         ss = octet_sum(ss);
-        ct[h] = TRIG ? __expf(0.5f * ss * knorm_scale) : 1.f;
+        ct[h] = TRIG && !REV ? __expf(0.5f * ss * knorm_scale) : 1.f;
         hs[h] = 0.5f * LOG2E * ss * knorm_scale;
       }
       if (task < NQT) {
         *(u32x4*)&Qs[buf][k_index(task >> 3, task & 7)] = r.d[k][0];
-        if (POS && (task & 7) == 0) Hq[buf][task >> 3] = hs[0];
+        if (QOFF && (task & 7) == 0) Hq[buf][task >> 3] = hs[0];
       } else if (task < NTASK) {
         const int kv = task - NQT;
         const int q = kv >> 3, c8 = kv & 7;
@@ -308,7 +329,8 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
         sc[mk][nq] = p;
       }
     }
-    // (g) causal mask (key <= query, diagonal kept) -> B fragments whose slot
+    // (g) causal mask (key <= query; >= when reversed; diagonal kept) ->
+    //     B fragments whose slot
     //     j <-> key token 16 (j / 4) + 4 g + j % 4, the value tile's order
     bf16x8 bs[2];
 #pragma unroll
@@ -317,7 +339,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int kt_tok = 16 * (j >> 2) + 4 * g + (j & 3), q_tok = 16 * nq + c;
-        v[j] = kt_tok <= q_tok ? sc[j >> 2][nq][j & 3] : 0.f;
+        v[j] = (REV ? kt_tok >= q_tok : kt_tok <= q_tok) ? sc[j >> 2][nq][j & 3] : 0.f;
       }
       bs[nq] = pack8(v);
     }
@@ -366,8 +388,9 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       for (int n = 0; n < 5; ++n) acc_s[ft][n] = mfma16(fk[ft], vf[n], acc_s[ft][n]);
   };
 
-  // Sum the waves' partial out^T tiles (mt < 4) and normalise by row 64.
-  auto reduce_store = [&](long long t0) {
+  // Sum the waves' partial out^T tiles (mt < 4) and normalise by row 64
+  // (C_AB: form a and the partial G . num; C_DV: scale by the weight).
+  auto reduce_store = [&](int buf, long long t0) {
     for (int tile = w; tile < 8; tile += NW) {
       const int mt = tile >> 1, nq = tile & 1;
       floatx4 num = {0.f, 0.f, 0.f, 0.f};
@@ -375,33 +398,69 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         num += *(const floatx4*)&Red[ww][((mt * 2 + nq) * 64 + lane) * 4];
-        den += Red[ww][((4 * 2 + nq) * 64 + c) * 4];
+        if (MODE != C_DV) den += Red[ww][((4 * 2 + nq) * 64 + c) * 4];
       }
       const long long tok = t0 + 16 * nq + c;
-      if (tok < seg1) {
-        const float inv = 1.0f / den;
+      const bool valid = tok < seg1;
+      const size_t off = head + (size_t)min(tok, (long long)L - 1) * D + 16 * mt + 4 * g;
+      float mul;
+      if (MODE == C_DV) mul = TRIG ? __builtin_amdgcn_exp2f(Hq[buf][16 * nq + c]) : 1.f;
+      else mul = 1.0f / den;
+      if (MODE == C_AB) {
+        // a = G / den; the tile's 16 columns of G . num, over the lane groups
+        const u32x2 raw = *(const u32x2*)(G + off);
+        const float gv[4] = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                             __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
+        float gn = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gn = fmaf(gv[r], num[r], gn);
+          num[r] = gv[r];
+        }
+        gn += __shfl_xor(gn, 16);
+        gn += __shfl_xor(gn, 32);
+        if (g == 0) {
+          Gp[MODE == C_AB ? mt : 0][16 * nq + c] = gn;
+          if (mt == 0) Inv[16 * nq + c] = mul;
+        }
+      }
+      if (valid) {
         u32x2 o;
-        o[0] = pack2(num[0] * inv, num[1] * inv);
-        o[1] = pack2(num[2] * inv, num[3] * inv);
-        *(u32x2*)(out + head + (size_t)tok * D + 16 * mt + 4 * g) = o;
+        o[0] = pack2(num[0] * mul, num[1] * mul);
+        o[1] = pack2(num[2] * mul, num[3] * mul);
+        *(u32x2*)(out + off) = o;
       }
     }
   };
+  // C_AB, after the barrier that follows reduce_store: b per token
+  auto store_b = [&](long long t0) {
+    if (MODE == C_AB && tid < CT && t0 + tid < seg1) {
+      const float gn = Gp[0][tid] + Gp[MODE == C_AB ? 1 : 0][tid] + Gp[MODE == C_AB ? 2 : 0][tid] +
+                       Gp[MODE == C_AB ? 3 : 0][tid];
+      const float inv = Inv[MODE == C_AB ? tid : 0];
+      bhat[(size_t)bh * L + t0 + tid] = -gn * inv * inv;
+    }
+  };
 
+  // chunks in token order, or from the last one when reversed
   const int n_chunks = (int)((seg1 - seg0 + CT - 1) / CT);
-  fetch(ra, seg0);
-  stage(ra, 0, seg0);
+  auto chunk_t0 = [&](int i) { return seg0 + (long long)(REV ? n_chunks - 1 - i : i) * CT; };
+  if (n_chunks > 0) {
+    fetch(ra, chunk_t0(0));
+    stage(ra, 0, chunk_t0(0));
+  }
   __syncthreads();
   for (int i = 0; i < n_chunks; ++i) {
     const int buf = i & 1;
-    const long long t0 = seg0 + (long long)i * CT;
+    const long long t0 = chunk_t0(i);
     const bool more = i + 1 < n_chunks;
-    if (more) fetch(ra, t0 + CT);
+    if (more) fetch(ra, chunk_t0(i + 1));
     compute(buf);
-    if (more) stage(ra, buf ^ 1, t0 + CT);
+    if (more) stage(ra, buf ^ 1, chunk_t0(i + 1));
     __syncthreads();
-    reduce_store(t0);
+    reduce_store(buf, t0);
     __syncthreads();
+    store_b(t0);
   }
 }
 
@@ -422,13 +481,35 @@ CausalPlan plan_causal(const Problem& p) {
   return cp;
 }
 
-template <int KIND, int NW>
+template <int KIND, int NW, int MODE>
 void launch_causal(const Problem& p, const Buffers& b, const CausalPlan& cp, const uint16_t* start,
-                   hipStream_t s, float oscale) {
-  hipLaunchKernelGGL((causal_kernel<KIND, NW>), dim3((unsigned)((long long)cp.keys.n_split * p.BH)),
+                   hipStream_t s, float oscale, const uint16_t* G, float* bhat) {
+  hipLaunchKernelGGL((causal_kernel<KIND, NW, MODE>), dim3((unsigned)((long long)cp.keys.n_split * p.BH)),
                      dim3(NW * 64), 0, s, (const uint16_t*)b.q, (const uint16_t*)b.k,
                      (const uint16_t*)b.v, b.omega, start, (uint16_t*)b.out, p.L, cp.keys.seg_len,
-                     cp.keys.n_split, p.BH, oscale, 1.0f / sqrtf((float)D));
+                     cp.keys.n_split, p.BH, oscale, 1.0f / sqrtf((float)D), G, bhat);
+}
+
+template <int KIND, int MODE = C_OUT>
+void launch_causal_m(const Problem& p, const Buffers& b, const CausalPlan& cp, const uint16_t* start,
+                     hipStream_t s, float oscale, const uint16_t* G = nullptr, float* bhat = nullptr) {
+  switch (p.m / 32) {
+    case 1: launch_causal<KIND, 1, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 2: launch_causal<KIND, 2, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 3: launch_causal<KIND, 3, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 4: launch_causal<KIND, 4, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 5: launch_causal<KIND, 5, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 6: launch_causal<KIND, 6, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    case 7: launch_causal<KIND, 7, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+    default: launch_causal<KIND, 8, MODE>(p, b, cp, start, s, oscale, G, bhat); break;
+  }
+}
+
+void launch_scan(const Problem& p, const CausalPlan& cp, const uint16_t* part, uint16_t* start,
+                 bool rev, hipStream_t s) {
+  const long long per_seg8 = p.BH * (long long)state_elems(p.F) / 8;
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s, part,
+                     start, cp.keys.n_split, per_seg8, rev ? 1 : 0);
 }
 
 template <int KIND>
@@ -442,29 +523,130 @@ hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, Ph
   for (int r = 0; r < reps; ++r) launch_kv_nw<KIND>(p, b, cp.keys, nullptr, s, oscale);
   phase_end(hook, s, reps);
 
-  const long long per_seg8 = p.BH * (long long)state_elems(p.F) / 8;
   phase_begin(hook, s, "mfma_state_scan");
-  for (int r = 0; r < reps; ++r)
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per_seg8 + 255) / 256)), dim3(256), 0, s,
-                       (const uint16_t*)b.ws, start, cp.keys.n_split, per_seg8);
+  for (int r = 0; r < reps; ++r) launch_scan(p, cp, (const uint16_t*)b.ws, start, false, s);
   phase_end(hook, s, reps);
 
   phase_begin(hook, s, "mfma_causal_chunks");
-  for (int r = 0; r < reps; ++r) switch (p.m / 32) {
-    case 1: launch_causal<KIND, 1>(p, b, cp, start, s, oscale); break;
-    case 2: launch_causal<KIND, 2>(p, b, cp, start, s, oscale); break;
-    case 3: launch_causal<KIND, 3>(p, b, cp, start, s, oscale); break;
-    case 4: launch_causal<KIND, 4>(p, b, cp, start, s, oscale); break;
-    case 5: launch_causal<KIND, 5>(p, b, cp, start, s, oscale); break;
-    case 6: launch_causal<KIND, 6>(p, b, cp, start, s, oscale); break;
-    case 7: launch_causal<KIND, 7>(p, b, cp, start, s, oscale); break;
-    default: launch_causal<KIND, 8>(p, b, cp, start, s, oscale); break;
-  }
+  for (int r = 0; r < reps; ++r) launch_causal_m<KIND>(p, b, cp, start, s, oscale);
   phase_end(hook, s, reps);
   return hipGetLastError();
 }
 
+// Backward workspace: the forward partial and start states, a (bf16
+// [BH][L][64]) and b (float32 [BH][L]), the partial and start states of R.
+struct CausalBwdLayout {
+  CausalPlan cp;
+  size_t ab, bh, total;
+};
+
+CausalBwdLayout causal_bwd_layout(const Problem& p) {
+  CausalBwdLayout bl;
+  bl.cp = plan_causal(p);
+  bl.ab = align_up((size_t)p.BH * p.L * D * sizeof(uint16_t), 256);
+  bl.bh = align_up((size_t)p.BH * p.L * sizeof(float), 256);
+  bl.total = 2 * (bl.cp.keys.part_bytes + bl.cp.start_bytes) + bl.ab + bl.bh;
+  return bl;
+}
+
+// Gradients of causal attention (the chain rule of the forward pass, blog
+// page "用随机特征“骗”过 softmax...", section 核心机制：FAVOR+, causal variant):
+//   S_i = sum_{j <= i} u(k_j) v'_j^T, forward state, recomputed by segment;
+//   a_i, b_i from the recomputed forward (chunk kernel, C_AB);
+//   R_j = sum_{i >= j} u(q_i) [a_i, b_i]^T by segment, suffix-scanned;
+//   dQ, dK from the chunked gradient kernel (prefix S, suffix R);
+//   dV_j = c_j sum_{i >= j} (u(q_i) . u(k_j)) a_i (chunk kernel, C_DV).
+template <int KIND>
+hipError_t run_causal_backward_kind(const Problem& p, const Buffers& b, const BwdBuffers& gb,
+                                    hipStream_t s, PhaseHook* hook) {
+  const CausalBwdLayout bl = causal_bwd_layout(p);
+  const CausalPlan& cp = bl.cp;
+  const float oscale = omega_scale_for(KIND);
+  char* ws = (char*)b.ws;
+  uint16_t* partS = (uint16_t*)ws;
+  uint16_t* startS = (uint16_t*)(ws + cp.keys.part_bytes);
+  uint16_t* ab = (uint16_t*)((char*)startS + cp.start_bytes);
+  float* bhat = (float*)((char*)ab + bl.ab);
+  uint16_t* partR = (uint16_t*)((char*)bhat + bl.bh);
+  uint16_t* startR = (uint16_t*)((char*)partR + cp.keys.part_bytes);
+
+  // forward state by segment, and its prefix over segments
+  phase_begin(hook, s, "mfma_kv_state");
+  Buffers bk = b;
+  bk.ws = partS;
+  launch_kv_nw<KIND>(p, bk, cp.keys, nullptr, s, oscale);
+  launch_scan(p, cp, partS, startS, false, s);
+  phase_end(hook, s);
+  // a = g / den, b = -(g . num) / den^2 per query
+  phase_begin(hook, s, "mfma_bwd_ab");
+  Buffers bq = b;
+  bq.out = ab;
+  launch_causal_m<KIND, C_AB>(p, bq, cp, startS, s, oscale, (const uint16_t*)gb.dout, bhat);
+  phase_end(hook, s);
+  // R by segment (the key-side kernel on (Q, a) with b in column 64), and
+  // its suffix over segments
+  phase_begin(hook, s, "mfma_bwd_rstate");
+  Buffers br = b;
+  br.k = b.q;
+  br.v = ab;
+  br.ws = partR;
+  launch_kv_nw<KIND, true>(p, br, cp.keys, nullptr, s, oscale, bhat);
+  launch_scan(p, cp, partR, startR, true, s);
+  phase_end(hook, s);
+  CausalGradArgs ga;
+  ga.omega = b.omega;
+  ga.L = p.L;
+  ga.seg_len = cp.keys.seg_len;
+  ga.n_seg = cp.keys.n_split;
+  ga.BH = p.BH;
+  // dQ: X = Q with rows [a, b]; Y = K with rows c [v, 1]; prefix state S
+  phase_begin(hook, s, "mfma_bwd_dq");
+  ga.X = (const uint16_t*)b.q;
+  ga.W = ab;
+  ga.wz = bhat;
+  ga.Y = (const uint16_t*)b.k;
+  ga.Z = (const uint16_t*)b.v;
+  ga.zz = nullptr;
+  ga.start = startS;
+  ga.DX = (uint16_t*)gb.dq;
+  hipError_t e = launch_causal_grad(p, ga, false, s);
+  phase_end(hook, s);
+  if (e != hipSuccess) return e;
+  // dK: X = K with rows [v, 1]; Y = Q with rows [a, b]; suffix state R
+  phase_begin(hook, s, "mfma_bwd_dk");
+  ga.X = (const uint16_t*)b.k;
+  ga.W = (const uint16_t*)b.v;
+  ga.wz = nullptr;
+  ga.Y = (const uint16_t*)b.q;
+  ga.Z = ab;
+  ga.zz = bhat;
+  ga.start = startR;
+  ga.DX = (uint16_t*)gb.dk;
+  e = launch_causal_grad(p, ga, true, s);
+  phase_end(hook, s);
+  if (e != hipSuccess) return e;
+  // dV: the anti-causal numerator with queries K, keys Q and values a
+  phase_begin(hook, s, "mfma_bwd_dv");
+  Buffers bv = b;
+  bv.q = b.k;
+  bv.k = b.q;
+  bv.v = ab;
+  bv.out = gb.dv;
+  launch_causal_m<KIND, C_DV>(p, bv, cp, startR, s, oscale);
+  phase_end(hook, s);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t causal_backward_workspace_bytes(const Problem& p) { return causal_bwd_layout(p).total; }
+
+hipError_t run_causal_backward(const Problem& p, const Buffers& b, const BwdBuffers& g,
+                               hipStream_t s, PhaseHook* hook) {
+  if (p.kind == KIND_TRIG) return run_causal_backward_kind<KIND_TRIG>(p, b, g, s, hook);
+  if (p.kind == KIND_POS) return run_causal_backward_kind<KIND_POS>(p, b, g, s, hook);
+  return run_causal_backward_kind<KIND_RELU>(p, b, g, s, hook);
+}
 
 size_t causal_workspace_bytes(const Problem& p) {
   const CausalPlan cp = plan_causal(p);

@@ -508,5 +508,26 @@ inline void launch_kv_nw(const Problem& p, const Buffers& b, const Plan& pl, uin
   }
 }
 
+// Arguments of the causal gradient kernel (mfma_causal_grad.hip): X is the
+// side whose gradient DX is formed, with rows W and scalar column wz; Y the
+// other side, with rows Z and scalar column zz; start the bf16 state each
+// segment starts from ([n_seg][BH] states in the state layout).  Queries:
+// X = Q, W = a, wz = b, Y = K, Z = V, zz unused (the key weights); keys:
+// X = K, W = V, wz unused (1), Y = Q, Z = a, zz = b.
+struct CausalGradArgs {
+  const uint16_t* X;
+  const uint16_t* W;
+  const float* wz;
+  const uint16_t* Y;
+  const uint16_t* Z;
+  const float* zz;
+  const float* omega;
+  const uint16_t* start;
+  uint16_t* DX;
+  int L, seg_len, n_seg;
+  long long BH;
+};
+hipError_t launch_causal_grad(const Problem& p, const CausalGradArgs& a, bool keys, hipStream_t s);
+
 }  // namespace mfma
 }  // namespace favor

@@ -590,6 +590,9 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
 
 size_t causal_workspace_bytes(const Problem& p);
 hipError_t run_causal(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+size_t causal_backward_workspace_bytes(const Problem& p);
+hipError_t run_causal_backward(const Problem& p, const Buffers& b, const BwdBuffers& g,
+                               hipStream_t s, PhaseHook* hook);
 
 bool supports(const Problem& p) {
   return p.dtype == DT_BF16 && p.d == D && p.m % 32 == 0 && p.m >= 32 && p.m <= 256 &&
@@ -603,13 +606,16 @@ size_t workspace_bytes(const Problem& p) {
 }
 
 bool supports_backward(const Problem& p) {
-  return !p.causal && supports(p) && dphi_lds(p) <= 160 * 1024;
+  return supports(p) && (p.causal || dphi_lds(p) <= 160 * 1024);
 }
 
-size_t backward_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
+size_t backward_workspace_bytes(const Problem& p) {
+  return p.causal ? causal_backward_workspace_bytes(p) : bwd_layout(p).total;
+}
 
 hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
                         PhaseHook* hook) {
+  if (p.causal) return run_causal_backward(p, b, g, s, hook);
   if (p.kind == KIND_TRIG) return run_backward_kind<KIND_TRIG>(p, b, g, s, hook);
   if (p.kind == KIND_POS) return run_backward_kind<KIND_POS>(p, b, g, s, hook);
   return run_backward_kind<KIND_RELU>(p, b, g, s, hook);

@@ -182,9 +182,10 @@ def test_backward_workspace_covers_forward_state():
         fwd = F.favor_attention_workspace_bytes(*shape, causal, "generic")
         bwd = F.favor_attention_backward_workspace_bytes(*shape, causal, "generic")
         assert bwd > fwd
-    assert (F.favor_attention_backward_workspace_bytes(*shape, False, "mfma")
-            > F.favor_attention_workspace_bytes(*shape, False, "mfma"))
-    # the MFMA backward is bidirectional only
-    assert F.favor_attention_backward_workspace_bytes(*shape, True, "mfma") == 0
-    assert F.favor_attention_backward_resolve_path(1, 8, 4096, 64, 256, "bf16", "trig", True) == "generic"
-    assert F.favor_attention_backward_resolve_path(1, 8, 4096, 64, 256, "bf16", "trig", False) == "mfma"
+    for causal in (False, True):
+        assert (F.favor_attention_backward_workspace_bytes(*shape, causal, "mfma")
+                > F.favor_attention_workspace_bytes(*shape, causal, "mfma"))
+        assert F.favor_attention_backward_resolve_path(1, 8, 4096, 64, 256, "bf16", "trig", causal) == "mfma"
+    # outside the MFMA family (float32, or d != 64) the generic kernels run
+    assert F.favor_attention_backward_workspace_bytes(1, 8, 4096, 64, 256, "f32", "trig", True, "mfma") == 0
+    assert F.favor_attention_backward_resolve_path(1, 8, 4096, 32, 256, "bf16", "trig", True) == "generic"

@@ -103,11 +103,23 @@ def test_backward_mfma_many_splits():
     _check((1, 8, 32768, 64, 256, "bf16"), "trig", False, workers=O.default_workers(), paths=["mfma"])
 
 
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
+def test_backward_mfma_causal_headline_shape(kind):
+    # B4 H8 L4096 d64 m256 bf16 causal (16 segments of 256 tokens per head)
+    _check((4, 8, 4096, 64, 256, "bf16"), kind, True, workers=O.default_workers(), paths=["mfma"])
+
+
+def test_backward_mfma_causal_many_segments():
+    # two heads of 8192 tokens: 64 segments per head, so the prefix and
+    # suffix scans run over many segment states
+    _check((1, 2, 8192, 64, 256, "bf16"), "trig", True, workers=O.default_workers(), paths=["mfma"])
+
+
 def test_backward_config1():
     _check((1, 1, 512, 16, 64, "f32"), "trig", False)
 
 
-@pytest.mark.parametrize("causal,path", [(True, "generic"), (False, "mfma")])
+@pytest.mark.parametrize("causal,path", [(True, "generic"), (False, "mfma"), (True, "mfma")])
 def test_backward_workspace_contents_ignored(causal, path):
     shape = (1, 2, 300, 64, 256, "bf16")
     dev, (q, k, v), W, g_dev, g64 = _grad_problem(shape, "trig", causal, 3)
