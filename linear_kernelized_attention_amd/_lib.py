@@ -33,6 +33,7 @@ EXPORTS = (
     "favor_attention_workspace_bytes", "favor_attention_workspace_bytes_ex",
     "favor_attention", "favor_attention_ex", "favor_attention_resolve_path",
     "favor_profile_attention", "favor_embed_bf16", "favor_linear_bf16",
+    "favor_pack_weight_bf16", "favor_embed_linear_bf16",
     "favor_attention_backward_workspace_bytes", "favor_attention_backward",
     "favor_attention_backward_workspace_bytes_ex", "favor_attention_backward_ex",
 )
@@ -63,6 +64,8 @@ def _declare(lib: ctypes.CDLL) -> None:
         "favor_profile_attention": (i, [p, p, p, p, p] + [i] * 8 + [p, z, p, i, i, p, p, i, p]),
         "favor_embed_bf16": (i, [p, p, p, i, i, i, p]),
         "favor_linear_bf16": (i, [p, p, p, i, i, i, i, i, i, p]),
+        "favor_pack_weight_bf16": (i, [p, p, i, i, p]),
+        "favor_embed_linear_bf16": (i, [p, p, i, p, p, i, i, i, i, i, i, p]),
         "favor_attention_backward_workspace_bytes": (z, [i] * 8),
         "favor_attention_backward": (i, [p] * 8 + [i] * 8 + [p, z, p]),
         "favor_attention_backward_workspace_bytes_ex": (z, [i] * 9),
@@ -276,39 +279,95 @@ def favor_embed_bf16(ids, table, out=None):
     return out
 
 
-def favor_linear_bf16(x, w, M: int, N: int, K: int, in_heads: int = 0, out_heads: int = 0,
-                      seq_len: int = 0, out=None):
-    """Y = X W with optional head-split layouts (see include/favor.h)."""
+def favor_pack_weight_bf16(w, out=None):
+    """Wt = W^T for a bf16 [K, N] weight: the packed [N, K] layout of the
+    projections (a device layout change)."""
     import torch
-    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
-        raise TypeError("x and w must be bfloat16")
-    if not x.is_contiguous() or not w.is_contiguous():
-        raise ValueError("x and w must be contiguous")
-    if x.numel() != M * K or w.numel() != K * N:
-        raise ValueError("x must hold M*K and w K*N elements")
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous():
+        raise TypeError("w must be a contiguous 2-D bfloat16 tensor")
+    K, N = w.shape
+    if out is None:
+        out = torch.empty(N, K, dtype=torch.bfloat16, device=w.device)
+    elif out.numel() != K * N or not out.is_contiguous():
+        raise ValueError("out must be contiguous with K*N elements")
+    _check(lib().favor_pack_weight_bf16(w.data_ptr(), out.data_ptr(), K, N, _stream_ptr(w.device)),
+           "favor_pack_weight_bf16")
+    return out
+
+
+def favor_linear_bf16(x, wt, M: int, N: int, K: int, in_heads: int = 0, out_heads: int = 0,
+                      seq_len: int = 0, out=None):
+    """Y = X Wt^T with a packed [N, K] weight and optional head-split layouts
+    (see include/favor.h)."""
+    import torch
+    if x.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
+        raise TypeError("x and wt must be bfloat16")
+    if not x.is_contiguous() or not wt.is_contiguous():
+        raise ValueError("x and wt must be contiguous")
+    if x.numel() != M * K or wt.numel() != K * N:
+        raise ValueError("x must hold M*K and wt N*K elements")
     if out is None:
         out = torch.empty(M * N, dtype=torch.bfloat16, device=x.device)
     elif out.numel() != M * N:
         raise ValueError("out must hold M*N elements")
-    _check(lib().favor_linear_bf16(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, in_heads,
+    _check(lib().favor_linear_bf16(x.data_ptr(), wt.data_ptr(), out.data_ptr(), M, N, K, in_heads,
                                    out_heads, seq_len, _stream_ptr(x.device)), "favor_linear_bf16")
     return out
 
 
-def favor_performer_block(ids, embed, wq, wk, wv, wo, omega, heads: int, kind: str = "relu",
-                          path: str = "auto"):
-    """Masked-LM attention block: gather, Q/K/V projections written head-split,
-    FAVOR attention, output projection reading the head-split result."""
+def favor_embed_linear_bf16(ids, table, wt, out_heads: int = 0, head_dim: int = 0, seq_len: int = 0,
+                            out=None):
+    """Y = table[ids] Wt^T without storing table[ids]; head-split output in
+    groups of out_heads * head_dim columns (see include/favor.h)."""
     import torch
+    if ids.dtype != torch.int32 or table.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
+        raise TypeError("ids must be int32, table and wt bfloat16")
+    if not (ids.is_contiguous() and table.is_contiguous() and wt.is_contiguous()):
+        raise ValueError("ids, table and wt must be contiguous")
+    M = ids.numel()
+    vocab, K = table.shape
+    N = wt.shape[0]
+    if wt.numel() != N * K:
+        raise ValueError("wt must be [N, K] with K the table width")
+    if out is None:
+        out = torch.empty(M * N, dtype=torch.bfloat16, device=table.device)
+    elif out.numel() != M * N:
+        raise ValueError("out must hold M*N elements")
+    _check(lib().favor_embed_linear_bf16(ids.data_ptr(), table.data_ptr(), vocab, wt.data_ptr(),
+                                         out.data_ptr(), M, N, K, out_heads, head_dim, seq_len,
+                                         _stream_ptr(table.device)), "favor_embed_linear_bf16")
+    return out
+
+
+class BlockWeights:
+    """Packed projection weights of a masked-LM block: wqkv_t [3E, E] (the
+    Q, K and V weights' [out, in] rows stacked) and wo_t [E, E]."""
+
+    def __init__(self, wqkv_t, wo_t):
+        self.wqkv_t = wqkv_t
+        self.wo_t = wo_t
+
+
+def favor_block_weights(wq, wk, wv, wo) -> BlockWeights:
+    """Pack the block's four [E, E] (x W convention) weights once."""
+    import torch
+    E = wq.shape[0]
+    wqkv_t = torch.empty(3 * E, E, dtype=torch.bfloat16, device=wq.device)
+    for i, w in enumerate((wq, wk, wv)):
+        favor_pack_weight_bf16(w, out=wqkv_t[i * E:(i + 1) * E])
+    return BlockWeights(wqkv_t, favor_pack_weight_bf16(wo))
+
+
+def favor_performer_block(ids, embed, weights: BlockWeights, omega, heads: int, kind: str = "relu",
+                          path: str = "auto"):
+    """Masked-LM attention block: one fused gather + Q/K/V projection written
+    head-split, FAVOR attention, output projection reading the head-split
+    result."""
     B, L = ids.shape
     E = embed.shape[1]
     dh = E // heads
     M = B * L
-    x = favor_embed_bf16(ids, embed)
-    proj = []
-    for w in (wq, wk, wv):
-        y = favor_linear_bf16(x, w, M, E, E, 0, heads, L)
-        proj.append(y.view(B, heads, L, dh))
-    o = favor_attention(proj[0], proj[1], proj[2], omega, kind=kind, causal=False, path=path)
-    y = favor_linear_bf16(o, wo, M, E, E, heads, 0, L)
+    qkv = favor_embed_linear_bf16(ids, embed, weights.wqkv_t, heads, dh, L).view(3, B, heads, L, dh)
+    o = favor_attention(qkv[0], qkv[1], qkv[2], omega, kind=kind, causal=False, path=path)
+    y = favor_linear_bf16(o, weights.wo_t, M, E, E, heads, 0, L)
     return y.view(B, L, E)

@@ -1,26 +1,28 @@
-// Masked-LM attention block helpers: embedding gather and bf16 GEMM.
+// Masked-LM attention block kernels: embedding gather, weight packing and
+// the bf16 projections.
 //
 // The Performer block of the protein masked-LM ("Masked Language Modeling
 // for Proteins via Linearly Scalable Long-Context Transformers", summary
 // pages, Methodology / 实验设计) embeds token ids, projects them to
 // multi-head Q, K, V, runs FAVOR attention and projects the concatenated
-// heads back.  These kernels do the gather and the four projections so that
+// heads back.  These kernels do the gather and the projections so that
 // every arithmetic step of the block runs in this library.
 //
-// GEMM: Y[M, N] = X[M, K] W[K, N], bf16 operands, float32 accumulation on
-// v_mfma_f32_32x32x16_bf16, one round-to-nearest-even at the end.
-// Block tile 128 x 128 x 128, 8 waves in a 4 x 2 grid, each wave 32 x 64
-// (1 x 2 MFMA tiles).  The k loop is software-pipelined: loads run two k
-// tiles ahead in two register sets while the current tile is multiplied
-// out of one of two LDS buffers (a k tile of 128 is long enough to cover
-// the memory latency).  X tiles are staged row-major; W tiles are staged
-// transposed ([n][k]) -- a thread holds two k rows of eight columns and
-// writes (k, k + 1) pairs as 32-bit words -- so that each lane's eight
-// consecutive k values of an MFMA B fragment are one 16-byte LDS read.  The
-// result goes through LDS so that each lane stores 16 contiguous bytes.
-// Optional head-split layouts for X (gather) and Y (scatter) let the
-// projections read and write the [B, H, L, d] layout of the attention
-// kernels directly.
+// Projection: Y[M, N] = X[M, K] Wt[N, K]^T with the weight packed as
+// [out, in] rows (so that both operands stage with 16-byte copies), bf16
+// operands, float32 accumulation on v_mfma_f32_16x16x32_bf16, one
+// round-to-nearest-even at the end.  A block of 4 waves owns a 128 x BN
+// output tile (BN = 128 or 64), each wave 64 x BN/2, and streams K in steps
+// of 64 through two LDS buffers: the loads of step k + 1 are in flight in
+// registers while step k is multiplied, then stored to the other buffer;
+// one barrier per step.  Both tiles are stored with the 16-byte chunk ch of
+// row r at chunk ch ^ (r % 8), so that the fragment reads (16 rows x 4
+// chunks per instruction) and the staging writes are free of LDS bank
+// conflicts.  X rows come from a row-major matrix, from a head-split
+// [B, heads, L, K / heads] tensor, or from an embedding table indexed by
+// token ids (the gather fused into the projection); Y is stored row-major
+// or head-split, in groups of heads x head_dim columns (Q, K and V from one
+// launch).  The output tile is staged through LDS for 16-byte stores.
 #include "favor_internal.h"
 
 namespace favor {
@@ -28,8 +30,10 @@ namespace block {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// round to nearest even (lowers to v_cvt_pk_bf16_f32)
+__device__ inline uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // X[t] = table[ids[t]] (a zero row for ids outside [0, vocab)); one thread
 // per 16-byte chunk of a row (E a multiple of 8).
@@ -46,160 +50,281 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* ids, const uint16
   *(u32x4*)(x + (size_t)t * E + c8) = v;
 }
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int AROW = BK + 8, BROW = BK + 8;   // padded LDS rows (bf16 elements)
-constexpr int CROW = BN + 8;                  // padded LDS row of the staged result
+// Wt[n][k] = W[k][n] through a 64 x 64 LDS tile (padded rows); one block
+// of 256 threads per tile, bounds-checked for any K, N.
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W,
+                                                   uint16_t* __restrict__ Wt, int K, int N) {
+  __shared__ uint16_t t[64][65];
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int kk = e >> 6, nn = e & 63;
+    if (k0 + kk < K && n0 + nn < N) t[kk][nn] = W[(size_t)(k0 + kk) * N + n0 + nn];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int nn = e >> 6, kk = e & 63;
+    if (k0 + kk < K && n0 + nn < N) Wt[(size_t)(n0 + nn) * K + k0 + kk] = t[kk][nn];
+  }
+}
 
-// Transposed W tile: element (n, k) sits in 16-byte chunk (k / 8) ^ ((n / 8)
-// % 16) of row n, so that the staging writes (eight rows 8 apart per lane
-// group) and the fragment reads both spread over the LDS banks.
-__device__ inline int bt_col(int n, int k) { return (((k >> 3) ^ ((n >> 3) & 15)) << 3) | (k & 7); }
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
-// round to nearest even (lowers to v_cvt_pk_bf16_f32)
-__device__ inline uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+// sources of the X rows
+enum { XS_ROWS = 0, XS_HEADS = 1, XS_TABLE = 2 };
 
 struct GemmArgs {
-  const uint16_t* X;
-  const uint16_t* W;
+  const uint16_t* X;    // [M, K]; head-split [M / seq, in_heads, seq, K / in_heads]; or a table [vocab, K]
+  const int* ids;       // XS_TABLE: token ids [M]
+  const uint16_t* Wt;   // [N, K]
   uint16_t* Y;
-  int M, N, K, in_heads, out_heads, seq;
+  int M, N, K;
+  int in_heads, seq, vocab;
+  int out_heads, out_dh;   // 0: row-major Y; else groups of out_heads x out_dh columns
 };
 
-// Element offset of logical X[r][c] (c a multiple of 8 within one head).
-__device__ inline size_t x_offset(const GemmArgs& a, long long r, int c) {
-  if (a.in_heads == 0) return (size_t)r * a.K + c;
-  const int dh = a.K / a.in_heads;
-  const long long b = r / a.seq, t = r % a.seq;
-  const int h = c / dh, dc = c % dh;
-  return ((size_t)(b * a.in_heads + h) * a.seq + t) * dh + dc;
+constexpr int TBM = 128, TBK = 64, G_NT = 256;
+
+// LDS tile row r of 64 bf16 (eight 16-byte chunks): chunk ch at ch ^ (r % 8)
+__device__ inline int sw_index(int r, int ch) { return r * TBK + ((ch ^ (r & 7)) << 3); }
+
+// Blocks are dispatched round-robin over the 8 XCDs; renumber them so that
+// consecutive logical tiles (the column tiles of one row band, which read
+// the same X rows) run on one XCD and share its L2.
+__device__ inline long long xcd_tile(long long b, long long total) {
+  if (total % 8) return b;
+  return (b % 8) * (total / 8) + b / 8;
 }
 
-// Element offset of logical Y[r][n] (n a multiple of 8 within one head).
-__device__ inline size_t y_offset(const GemmArgs& a, long long r, int n) {
-  if (a.out_heads == 0) return (size_t)r * a.N + n;
-  const int dh = a.N / a.out_heads;
-  const long long b = r / a.seq, t = r % a.seq;
-  const int h = n / dh, dn = n % dh;
-  return ((size_t)(b * a.out_heads + h) * a.seq + t) * dh + dn;
-}
+// NK > 0: K = 64 NK exactly, the k loop unrolled into straight-line code
+// (no loop-carried register sets and no branches, so the compiler waits for
+// exactly the loads a stage needs) with the loads PF steps ahead in PF
+// register sets; NK == 0: any K, a runtime loop two steps ahead.
+template <int XS, int WN, int NK, int PF>
+__global__ __launch_bounds__(G_NT, 2) void gemm_kernel(GemmArgs a) {
+  constexpr int TBN = 32 * WN;   // block columns; each wave 64 x 16 WN
+  // two k-step buffers of X and Wt; reused for the output tile at the end
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (TBM + TBN) * TBK];
+  uint16_t* As = lds;                    // [2][TBM * TBK]
+  uint16_t* Bs = lds + 2 * TBM * TBK;    // [2][TBN * TBK]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int wr = w >> 1, wc = w & 1;
+  const int ntn = (a.N + TBN - 1) / TBN;
+  const long long lb = xcd_tile(blockIdx.x, gridDim.x);
+  const long long m0 = (lb / ntn) * TBM;
+  const int n0 = (int)(lb % ntn) * TBN;
 
-constexpr int GEMM_NT = 512;   // 8 waves: 4 (rows) x 2 (columns), each 32 x 64
-
-__global__ __launch_bounds__(GEMM_NT) void gemm_kernel(GemmArgs a) {
-  // two k-tile buffers of X (row-major) and W (transposed); reused for the
-  // staged result after the k loop
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM * AROW + BN * BROW)];
-  uint16_t (*As)[BM][AROW] = reinterpret_cast<uint16_t (*)[BM][AROW]>(lds);
-  uint16_t (*Bt)[BN][BROW] = reinterpret_cast<uint16_t (*)[BN][BROW]>(lds + 2 * BM * AROW);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const long long m0 = (long long)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-
-  floatx16 acc[2];
+  // staging: thread tid moves chunk tid % 8 of tile rows tid / 8 + 32 i
+  constexpr int NA = TBM * 8 / G_NT, NB = TBN * 8 / G_NT;
+  const int ch = tid & 7, r0 = tid >> 3;
+  // Per staged row: the start of its X row (XS_HEADS: of its token's row in
+  // head 0, the heads being seq * dh elements apart) and whether it exists.
+  // The loads themselves are unconditional (rows past the end read row 0,
+  // k past the end the last chunk) and the masks are applied when the
+  // registers are stored to LDS: a load under a divergent branch would make
+  // the compiler wait for every load in flight, prefetches included.
+  const uint16_t* asrc[NA];
+  bool aok[NA];
+  const int dh_in = XS == XS_HEADS ? a.K / a.in_heads : 1;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-
-  // loads of a k tile: threads 0..255 take X rows xr0 + 16 h (h = 0..7),
-  // columns xc8..+7; threads 256..511 take W row pairs (k) 2 (wk2 + 16 q),
-  // 2 (wk2 + 16 q) + 1 (q = 0..3), columns wn8..+7.  Loads past K read 0.
-  // Two register sets keep the loads two k tiles ahead.
-  constexpr int NL = 8;   // 16-byte loads per thread per k tile
-  const bool xload = tid < 256;
-  const int lt = tid & 255;
-  const int xr0 = lt >> 4, xc8 = (lt & 15) * 8;
-  const int wk2 = lt >> 4, wn8 = (lt & 15) * 8;
-  u32x4 rg[2][NL];
-  auto fetch = [&](u32x4 (&r)[NL], int k0) {
-#pragma unroll
-    for (int h = 0; h < NL; ++h) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      if (xload) {
-        const long long row = m0 + xr0 + 16 * h;
-        const int c = k0 + xc8;
-        r[h] = (row < a.M && c < a.K) ? *(const u32x4*)(a.X + x_offset(a, row, c)) : zero;
-      } else {
-        const int kr = k0 + 2 * (wk2 + 16 * (h >> 1)) + (h & 1);
-        r[h] = (kr < a.K && n0 + wn8 < a.N) ? *(const u32x4*)(a.W + (size_t)kr * a.N + n0 + wn8) : zero;
+  for (int i = 0; i < NA; ++i) {
+    const long long r = m0 + r0 + 32 * i;
+    asrc[i] = a.X;
+    aok[i] = r < a.M;
+    if (aok[i]) {
+      if (XS == XS_ROWS) asrc[i] = a.X + (size_t)r * a.K;
+      if (XS == XS_TABLE) {
+        const int id = a.ids[r];
+        aok[i] = id >= 0 && id < a.vocab;
+        if (aok[i]) asrc[i] = a.X + (size_t)id * a.K;
+      }
+      if (XS == XS_HEADS) {
+        const int b = (int)r / a.seq, t = (int)r % a.seq;
+        asrc[i] = a.X + ((size_t)b * a.in_heads * a.seq + t) * dh_in;
       }
     }
+  }
+  const uint16_t* bsrc[NB];
+  bool bok[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + r0 + 32 * i;
+    bok[i] = n < a.N;
+    bsrc[i] = a.Wt + (size_t)(bok[i] ? n : 0) * a.K;
+  }
+  // two register sets keep the loads two k steps ahead of the products
+  struct Regs {
+    u32x4 a[NA], b[NB];
+    bool kok;
   };
-  auto stage = [&](const u32x4 (&r)[NL], int buf) {
-    if (xload) {
-#pragma unroll
-      for (int h = 0; h < NL; ++h) *(u32x4*)&As[buf][xr0 + 16 * h][xc8] = r[h];
-    } else {
-#pragma unroll
-      for (int q = 0; q < NL / 2; ++q) {
-        const uint16_t* w0 = (const uint16_t*)&r[2 * q];
-        const uint16_t* w1 = (const uint16_t*)&r[2 * q + 1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *(uint32_t*)&Bt[buf][wn8 + i][bt_col(wn8 + i, 2 * (wk2 + 16 * q))] =
-              (uint32_t)w0[i] | ((uint32_t)w1[i] << 16);
+  Regs rs[PF > 2 ? PF : 2];
+  // XS_HEADS: head and in-head column of this thread's chunk, advanced by
+  // 64 columns per fetch (the fetches run in k order)
+  int kh = 0, kd = 8 * ch;
+  if (XS == XS_HEADS) {
+    kh = kd / dh_in;
+    kd -= kh * dh_in;
+  }
+  auto fetch = [&](Regs& rg, int k0) {
+    const int k = k0 + 8 * ch;
+    const int kc = min(k, a.K - 8);
+    rg.kok = k < a.K;
+    // XS_HEADS: the chunk's offset within a token's head-split row (any
+    // valid offset once past K: the chunk is masked)
+    size_t koff = (size_t)kc;
+    if (XS == XS_HEADS) {
+      koff = rg.kok ? (size_t)kh * a.seq * dh_in + kd : 0;
+      kd += TBK;
+      while (kd >= dh_in) {
+        kd -= dh_in;
+        ++kh;
       }
     }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) rg.a[i] = *(const u32x4*)(asrc[i] + koff);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rg.b[i] = *(const u32x4*)(bsrc[i] + kc);
   };
+  auto stage = [&](const Regs& rg, int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *(u32x4*)&As[buf * TBM * TBK + sw_index(r0 + 32 * i, ch)] = (aok[i] && rg.kok) ? rg.a[i] : zero;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      *(u32x4*)&Bs[buf * TBN * TBK + sw_index(r0 + 32 * i, ch)] = (bok[i] && rg.kok) ? rg.b[i] : zero;
+  };
+
+  // acc[i][j]: rows 64 wr + 16 i + 4 g + r, columns 16 WN wc + 16 j + c
+  floatx4 acc[4][WN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
+    const uint16_t* at = As + buf * TBM * TBK;
+    const uint16_t* bt = Bs + buf * TBN * TBK;
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      const int kk = ks + 8 * (lane >> 5);
-      const bf16x8 af = *(const bf16x8*)&As[buf][wr * 32 + (lane & 31)][kk];
-      bf16x8 bfr[2];
+    for (int s = 0; s < TBK / 32; ++s) {
+      bf16x8 af[4], bf[WN];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wc * 64 + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8*)&Bt[buf][n][bt_col(n, kk)];
-      }
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)&at[sw_index(64 * wr + 16 * i + c, 4 * s + g)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
+      for (int j = 0; j < WN; ++j)
+        bf[j] = *(const bf16x8*)&bt[sw_index(16 * WN * wc + 16 * j + c, 4 * s + g)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  const int nk = (a.K + BK - 1) / BK;
-  fetch(rg[0], 0);
-  if (nk > 1) fetch(rg[1], BK);
-  stage(rg[0], 0);
+  // step kt: its tile is in LDS buffer kt % 2; the loads of step kt + 1 are
+  // in register set (kt + 1) % 2, and set kt % 2 (staged during step
+  // kt - 1) takes the loads of step kt + 2
+  if constexpr (NK > 0) {
+    // step kt: its tile is in LDS buffer kt % 2; register set kt % PF,
+    // staged during step kt - 1, takes the loads of step kt + PF
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < NK) fetch(rs[p], p * TBK);
+    stage(rs[0], 0);
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      if (kt + PF < NK) fetch(rs[kt % PF], (kt + PF) * TBK);
+      compute(kt & 1);
+      if (kt + 1 < NK) stage(rs[(kt + 1) % PF], (kt + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+  const int nk = (a.K + TBK - 1) / TBK;
+  fetch(rs[0], 0);
+  if (nk > 1) fetch(rs[1], TBK);
+  stage(rs[0], 0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    // even step: tile kt in buffer 0; set 0 is free, set 1 holds tile kt + 1
-    if (kt + 2 < nk) fetch(rg[0], (kt + 2) * BK);
+    fetch(rs[0], (kt + 2) * TBK);   // past the end: clamped loads, never staged
     compute(0);
-    if (kt + 1 < nk) stage(rg[1], 1);
+    if (kt + 1 < nk) stage(rs[1], 1);
     __syncthreads();
     if (kt + 1 >= nk) break;
-    // odd step: tile kt + 1 in buffer 1; set 0 holds tile kt + 2
-    if (kt + 3 < nk) fetch(rg[1], (kt + 3) * BK);
+    fetch(rs[1], (kt + 3) * TBK);
     compute(1);
-    if (kt + 2 < nk) stage(rg[0], 0);
+    if (kt + 2 < nk) stage(rs[0], 0);
     __syncthreads();
   }
+  }
 
-  // C layout (32x32): lane holds column lane % 32 and rows
-  // 8 (r / 4) + 4 (lane / 32) + r % 4 for r = 0..15.  Stage the bf16 tile
-  // in LDS, then store rows of 128 columns as 16-byte chunks.
-  uint16_t (*Cs)[CROW] = reinterpret_cast<uint16_t (*)[CROW]>(lds);
+  // output tile in LDS (bf16 [TBM][TBN + 8]), then 16-byte stores
+  constexpr int CROW = TBN + 8;
+  uint16_t* Cs = lds;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = wc * 64 + j * 32 + (lane & 31);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      Cs[row][col] = f32_to_bf16_rne(acc[j][r]);
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Cs[(64 * wr + 16 * i + 4 * g + r) * CROW + 16 * WN * wc + 16 * j + c] =
+            f32_to_bf16_rne(acc[i][j][r]);
+  __syncthreads();
+  // Each thread stores one 8-column chunk of rows row0, row0 + RSTEP, ...:
+  // the chunk's column offset is fixed, the rows' (batch, token) advance
+  // without divisions.
+  constexpr int CPR = TBN / 8, RSTEP = G_NT / CPR;
+  const int c8 = (tid % CPR) * 8, row0 = tid / CPR;
+  const int n = n0 + c8;
+  if (n < a.N) {
+    size_t coff = (size_t)n;
+    int dh = 1;
+    if (a.out_heads > 0) {
+      dh = a.out_dh;
+      const int gw = a.out_heads * dh, grp = n / gw, h = (n % gw) / dh;
+      coff = (size_t)grp * a.M * gw + (size_t)h * a.seq * dh + n % dh;
+    }
+    const long long r0 = m0 + row0;
+    int b = 0, t = 0;
+    if (a.out_heads > 0) {
+      b = (int)(r0 / a.seq);
+      t = (int)(r0 - (long long)b * a.seq);
+    }
+#pragma unroll
+    for (int it = 0; it < TBM / RSTEP; ++it) {
+      const long long r = r0 + it * RSTEP;
+      if (r < a.M) {
+        const size_t off = a.out_heads > 0 ? coff + ((size_t)b * a.out_heads * a.seq + t) * dh
+                                           : (size_t)r * a.N + coff;
+        *(u32x4*)(a.Y + off) = *(const u32x4*)&Cs[(row0 + it * RSTEP) * CROW + c8];
+      }
+      if (a.out_heads > 0) {
+        t += RSTEP;
+        while (t >= a.seq) {
+          t -= a.seq;
+          ++b;
+        }
+      }
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < BM * BN / 8 / GEMM_NT; ++it) {
-    const int ch = tid + it * GEMM_NT;
-    const int row = ch >> 4, c8 = (ch & 15) * 8;
-    const long long r = m0 + row;
-    if (r < a.M && n0 + c8 < a.N)
-      *(u32x4*)(a.Y + y_offset(a, r, n0 + c8)) = *(const u32x4*)&Cs[row][c8];
-  }
+}
+
+constexpr int GEMM_PF = 2;   // prefetch depth of the unrolled k loop (3 and 4 measured no faster)
+
+template <int XS, int WN>
+void launch_gemm_w(const GemmArgs& a, long long blocks, hipStream_t s) {
+  if (a.K == 8 * TBK)
+    hipLaunchKernelGGL((gemm_kernel<XS, WN, 8, GEMM_PF>), dim3((unsigned)blocks), dim3(G_NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<XS, WN, 0, 2>), dim3((unsigned)blocks), dim3(G_NT), 0, s, a);
+}
+
+template <int XS>
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  // 128-column tiles when they give at least two tiles per CU, else 64
+  const long long mt = (a.M + TBM - 1) / TBM;
+  if (mt * ((a.N + 127) / 128) >= 512) launch_gemm_w<XS, 4>(a, mt * ((a.N + 127) / 128), s);
+  else launch_gemm_w<XS, 2>(a, mt * ((a.N + 63) / 64), s);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -212,12 +337,24 @@ hipError_t embed(const int* ids, const uint16_t* table, uint16_t* x, int n_tok, 
   return hipGetLastError();
 }
 
-hipError_t linear(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K,
-                  int in_heads, int out_heads, int seq_len, hipStream_t s) {
-  GemmArgs a{X, W, Y, M, N, K, in_heads, out_heads, seq_len};
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(GEMM_NT), 0, s, a);
+hipError_t pack_weight(const uint16_t* W, uint16_t* Wt, int K, int N, hipStream_t s) {
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256), 0, s,
+                     W, Wt, K, N);
   return hipGetLastError();
+}
+
+hipError_t linear(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
+                  int in_heads, int out_heads, int seq_len, hipStream_t s) {
+  GemmArgs a{X, nullptr, Wt, Y, M, N, K, in_heads, seq_len, 0, out_heads,
+             out_heads > 0 ? N / out_heads : 0};
+  return in_heads > 0 ? launch_gemm<XS_HEADS>(a, s) : launch_gemm<XS_ROWS>(a, s);
+}
+
+hipError_t embed_linear(const int* ids, const uint16_t* table, int vocab, const uint16_t* Wt,
+                        uint16_t* Y, int M, int N, int K, int out_heads, int head_dim, int seq_len,
+                        hipStream_t s) {
+  GemmArgs a{table, ids, Wt, Y, M, N, K, 0, seq_len, vocab, out_heads, head_dim};
+  return launch_gemm<XS_TABLE>(a, s);
 }
 
 }  // namespace block

@@ -326,23 +326,53 @@ int favor_embed_bf16(const int* ids, const void* table, void* x, int n_tok, int 
   return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
-int favor_linear_bf16(const void* X, const void* W, void* Y, int M, int N, int K, int in_heads,
+int favor_pack_weight_bf16(const void* W, void* Wt, int K, int N, void* stream) {
+  if (K < 1 || N < 1 || !W || !Wt) return FAVOR_ERR_INVALID_ARG;
+  if ((long long)K * N > (1LL << 40)) return FAVOR_ERR_UNSUPPORTED;
+  if (overlaps(Wt, (size_t)K * N * 2, W, (size_t)K * N * 2)) return FAVOR_ERR_ALIAS;
+  hipError_t e = favor::block::pack_weight((const uint16_t*)W, (uint16_t*)Wt, K, N, (hipStream_t)stream);
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+int favor_linear_bf16(const void* X, const void* Wt, void* Y, int M, int N, int K, int in_heads,
                       int out_heads, int seq_len, void* stream) {
   if (M < 1 || N < 1 || K < 1 || in_heads < 0 || out_heads < 0) return FAVOR_ERR_INVALID_ARG;
-  if (!X || !W || !Y) return FAVOR_ERR_INVALID_ARG;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return FAVOR_ERR_INVALID_ARG;
-  if (N % 32 || K % 32) return FAVOR_ERR_UNSUPPORTED;
+  if (!X || !Wt || !Y) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Wt) || !aligned16(Y)) return FAVOR_ERR_INVALID_ARG;
+  if (N % 8 || K % 8) return FAVOR_ERR_UNSUPPORTED;
   if (in_heads > 0 || out_heads > 0) {
     if (seq_len < 1 || M % seq_len) return FAVOR_ERR_INVALID_ARG;
-    if (in_heads > 0 && K % (32 * in_heads)) return FAVOR_ERR_UNSUPPORTED;
-    if (out_heads > 0 && N % (32 * out_heads)) return FAVOR_ERR_UNSUPPORTED;
+    if (in_heads > 0 && K % (8 * in_heads)) return FAVOR_ERR_UNSUPPORTED;
+    if (out_heads > 0 && N % (8 * out_heads)) return FAVOR_ERR_UNSUPPORTED;
   }
   if ((long long)M * N > (1LL << 40) || (long long)M * K > (1LL << 40)) return FAVOR_ERR_UNSUPPORTED;
   if (overlaps(Y, (size_t)M * N * 2, X, (size_t)M * K * 2) ||
-      overlaps(Y, (size_t)M * N * 2, W, (size_t)K * N * 2))
+      overlaps(Y, (size_t)M * N * 2, Wt, (size_t)K * N * 2))
     return FAVOR_ERR_ALIAS;
-  hipError_t e = favor::block::linear((const uint16_t*)X, (const uint16_t*)W, (uint16_t*)Y, M, N, K,
+  hipError_t e = favor::block::linear((const uint16_t*)X, (const uint16_t*)Wt, (uint16_t*)Y, M, N, K,
                                       in_heads, out_heads, seq_len, (hipStream_t)stream);
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+int favor_embed_linear_bf16(const int* ids, const void* table, int vocab, const void* Wt, void* Y,
+                            int M, int N, int K, int out_heads, int head_dim, int seq_len,
+                            void* stream) {
+  if (M < 1 || N < 1 || K < 1 || vocab < 1 || out_heads < 0) return FAVOR_ERR_INVALID_ARG;
+  if (!ids || !table || !Wt || !Y) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(table) || !aligned16(Wt) || !aligned16(Y)) return FAVOR_ERR_INVALID_ARG;
+  if (N % 8 || K % 8) return FAVOR_ERR_UNSUPPORTED;
+  if (out_heads > 0) {
+    if (seq_len < 1 || M % seq_len || head_dim < 1) return FAVOR_ERR_INVALID_ARG;
+    if (head_dim % 8 || N % (out_heads * head_dim)) return FAVOR_ERR_UNSUPPORTED;
+  }
+  if ((long long)M * N > (1LL << 40) || (long long)vocab * K > (1LL << 40)) return FAVOR_ERR_UNSUPPORTED;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlaps(Y, yb, table, (size_t)vocab * K * 2) || overlaps(Y, yb, Wt, (size_t)K * N * 2) ||
+      overlaps(Y, yb, ids, (size_t)M * 4))
+    return FAVOR_ERR_ALIAS;
+  hipError_t e = favor::block::embed_linear(ids, (const uint16_t*)table, vocab, (const uint16_t*)Wt,
+                                            (uint16_t*)Y, M, N, K, out_heads, head_dim, seq_len,
+                                            (hipStream_t)stream);
   return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 

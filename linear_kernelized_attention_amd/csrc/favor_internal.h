@@ -99,8 +99,12 @@ hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofra
 namespace block {
 hipError_t embed(const int* ids, const uint16_t* table, uint16_t* x, int n_tok, int vocab, int E,
                  hipStream_t s);
-hipError_t linear(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K,
+hipError_t pack_weight(const uint16_t* W, uint16_t* Wt, int K, int N, hipStream_t s);
+hipError_t linear(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
                   int in_heads, int out_heads, int seq_len, hipStream_t s);
+hipError_t embed_linear(const int* ids, const uint16_t* table, int vocab, const uint16_t* Wt,
+                        uint16_t* Y, int M, int N, int K, int out_heads, int head_dim, int seq_len,
+                        hipStream_t s);
 }  // namespace block
 
 }  // namespace favor

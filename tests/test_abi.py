@@ -120,7 +120,8 @@ def test_resolve_path():
 def test_linear_and_embed_argument_checks():
     lib = F.lib()
     assert lib.favor_linear_bf16(QA, KA, OA, 0, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
-    assert lib.favor_linear_bf16(QA, KA, OA, 64, 48, 64, 0, 0, 0, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_linear_bf16(QA, KA, OA, 64, 44, 64, 0, 0, 0, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_linear_bf16(QA, KA, OA, 64, 64, 64, 0, 3, 64, None) == B.FAVOR_ERR_UNSUPPORTED
     assert lib.favor_linear_bf16(QA, KA, QA, 64, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_ALIAS
     assert lib.favor_linear_bf16(QA, KA, OA, 100, 64, 64, 0, 2, 64, None) == B.FAVOR_ERR_INVALID_ARG
     assert lib.favor_embed_bf16(0, KA, OA, 10, 26, 512, None) == B.FAVOR_ERR_INVALID_ARG
@@ -128,6 +129,19 @@ def test_linear_and_embed_argument_checks():
     assert lib.favor_embed_bf16(QA, KA, OA, 10, 26, 12, None) == B.FAVOR_ERR_UNSUPPORTED
     assert lib.favor_embed_bf16(QA, KA + 2, OA, 10, 26, 512, None) == B.FAVOR_ERR_INVALID_ARG
     assert lib.favor_linear_bf16(QA + 2, KA, OA, 64, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
+    # weight packing
+    assert lib.favor_pack_weight_bf16(QA, OA, 0, 64, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_pack_weight_bf16(QA, 0, 64, 64, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_pack_weight_bf16(QA, QA + 64, 64, 64, None) == B.FAVOR_ERR_ALIAS
+    # fused gather + projection: ids, table, vocab, Wt, Y, M, N, K, heads, head_dim, seq
+    ids = QA + (1 << 26)
+    assert lib.favor_embed_linear_bf16(0, KA, 26, VA, OA, 64, 192, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_embed_linear_bf16(ids, KA, 0, VA, OA, 64, 192, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_embed_linear_bf16(ids, KA, 26, VA, OA, 64, 196, 64, 0, 0, 0, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_embed_linear_bf16(ids, KA, 26, VA, OA, 64, 192, 64, 2, 36, 32, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_embed_linear_bf16(ids, KA, 26, VA, OA, 64, 200, 64, 2, 32, 32, None) == B.FAVOR_ERR_UNSUPPORTED
+    assert lib.favor_embed_linear_bf16(ids, KA, 26, VA, OA, 60, 192, 64, 2, 32, 32, None) == B.FAVOR_ERR_INVALID_ARG
+    assert lib.favor_embed_linear_bf16(ids, KA, 26, VA, KA, 64, 192, 64, 0, 0, 0, None) == B.FAVOR_ERR_ALIAS
 
 
 @pytest.mark.parametrize("m,d", [(64, 16), (256, 64), (40, 16)])

@@ -24,8 +24,11 @@ def test_embed_exact():
 @pytest.mark.parametrize("M,N,K,ih,oh,seq", [
     (8192, 512, 512, 0, 8, 4096),     # Q/K/V projection, head-split output
     (8192, 512, 512, 8, 0, 4096),     # output projection, head-split input
+    (8192, 1536, 512, 0, 0, 0),       # 128-column tiles
     (300, 96, 64, 0, 0, 0),           # ragged rows, N not a multiple of the tile
+    (257, 200, 136, 0, 0, 0),         # K not a multiple of the 64-wide k step
     (1, 32, 32, 0, 0, 0),
+    (1, 8, 8, 0, 0, 0),
 ])
 def test_linear(M, N, K, ih, oh, seq):
     r = np.random.default_rng(M + N)
@@ -37,7 +40,10 @@ def test_linear(M, N, K, ih, oh, seq):
         Xd = X.reshape(Bb, seq, ih, K // ih).transpose(0, 2, 1, 3).copy()
     else:
         Xd = X
-    y = F.favor_linear_bf16(to_device(Xd, "bf16"), to_device(W, "bf16"), M, N, K, ih, oh, seq)
+    wt = F.favor_pack_weight_bf16(to_device(W, "bf16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(wt.view(torch.int16).cpu().numpy().view(np.uint16), W.T)
+    y = F.favor_linear_bf16(to_device(Xd, "bf16"), wt, M, N, K, ih, oh, seq)
     torch.cuda.synchronize()
     y = from_device(y)
     ref = X64 @ W64
@@ -59,9 +65,10 @@ def test_performer_block_config5():
                             kind="relu", workers=O.default_workers())
     omega = torch.from_numpy(F.favor_orf_omega(dr.gaussian, dr.radii, cfg["m"])).cuda()
     dev = [to_device(x, "bf16") for x in (b.embed, b.wq, b.wk, b.wv, b.wo)]
+    weights = F.favor_block_weights(*dev[1:])
     ids = torch.from_numpy(b.ids).cuda()
     for path in ("generic", "auto"):
-        y = F.favor_performer_block(ids, *dev, omega, heads=cfg["H"], kind="relu", path=path)
+        y = F.favor_performer_block(ids, dev[0], weights, omega, heads=cfg["H"], kind="relu", path=path)
         torch.cuda.synchronize()
         y = from_device(y)
         for bi in range(cfg["B"]):
@@ -73,3 +80,33 @@ def test_performer_block_config5():
         for t in (0, 5, 25):
             rows = y[0, ids0 == t]
             assert np.allclose(rows, rows[:1], atol=1e-6)
+
+
+@pytest.mark.parametrize("M,N,K,heads,hd,seq,vocab", [
+    (8192, 1536, 512, 8, 64, 4096, 26),   # the block's fused Q, K, V projection
+    (300, 96, 64, 2, 16, 100, 7),         # ragged rows, 3 groups of 2 x 16
+    (130, 40, 24, 0, 0, 0, 5),            # row-major output
+])
+def test_embed_linear(M, N, K, heads, hd, seq, vocab):
+    r = np.random.default_rng(M + N + K)
+    table, T64 = I.to_storage(r.standard_normal((vocab, K)) * 0.5, "bf16")
+    W, W64 = I.to_storage(r.standard_normal((K, N)) * 0.05, "bf16")
+    ids = r.integers(-2, vocab + 2, size=M).astype(np.int32)   # some ids out of range: zero rows
+    wt = F.favor_pack_weight_bf16(to_device(W, "bf16"))
+    y = F.favor_embed_linear_bf16(torch.from_numpy(ids).cuda(), to_device(table, "bf16"), wt, heads, hd, seq)
+    torch.cuda.synchronize()
+    y = from_device(y)
+    X64 = np.where(((ids >= 0) & (ids < vocab))[:, None], T64[np.clip(ids, 0, vocab - 1)], 0.0)
+    ref = X64 @ W64
+    if heads:
+        G = heads * hd
+        Bb = M // seq
+        # [N / G, B, heads, seq, hd] -> [M, N]
+        y = y.reshape(N // G, Bb, heads, seq, hd).transpose(1, 3, 0, 2, 4).reshape(M, N)
+    else:
+        y = y.reshape(M, N)
+    err = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert err <= 4e-3, err
+    # rows of out-of-range ids are exactly zero
+    bad = (ids < 0) | (ids >= vocab)
+    assert np.all(y[bad] == 0)
