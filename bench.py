@@ -277,6 +277,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    # instead of the throughput line: the estimator-quality sweep (error of
+    # the GPU output against exact softmax over m and feature kinds)
+    ap.add_argument("--estimator-sweep", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -293,6 +296,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.estimator_sweep:
+        from linear_kernelized_attention_amd import sweep
+        print(json.dumps(sweep.run()), flush=True)
+        return
     if args.calibrate_copy:
         nbytes = calibrate_copy()
         print(json.dumps({"copy_calibration_bytes_read": nbytes}), flush=True)
