@@ -85,6 +85,9 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   // query-row exponent offsets: the positive map's, and log2 of the trig
   // weight that scales dV
   constexpr bool QOFF = POS || (TRIG && MODE == C_DV);
+  // value-column tiles: 4 of values and the z / denominator tile (C_DV
+  // needs no denominator and skips it)
+  constexpr int NMT = MODE == C_DV ? 4 : 5;
   constexpr int M = NW * 32;
   constexpr int F = TRIG ? 2 * M : M;
   constexpr int FT = TRIG ? 4 : 2;    // feature tiles of 16 per wave
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   auto om = [&](int ot, int kk) { return *(const bf16x8*)&Om[w][((ot * 2 + kk) * 64 + lane) * 8]; };
 
   // running state of this wave's features: S_w[f][col] as MFMA C fragments
-  floatx4 acc_s[FT][5];
+  floatx4 acc_s[FT][NMT];
   {
     const uint16_t* st = start + ((size_t)seg * BH + bh) * state_elems(F);
     auto ld4 = [&](const uint16_t* p) {
@@ -148,8 +151,10 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc_s[ft][n] = ld4(st + vtile_off(tile, n) + lane * 4);
       // column 64 (z) in lane group c = 0; the padding columns start at 0
-      const floatx4 z = ld4(st + z_off(F, 16 * tile + 4 * g));
-      acc_s[ft][4] = c == 0 ? z : floatx4{0.f, 0.f, 0.f, 0.f};
+      if (NMT == 5) {
+        const floatx4 z = ld4(st + z_off(F, 16 * tile + 4 * g));
+        acc_s[ft][NMT - 1] = c == 0 ? z : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   }
 
@@ -346,9 +351,9 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     // (h) partial out^T = S_prev,w^T phi_Q,w^T + V'^T (mask . Sc^T), one
     //     16-token query half at a time, written to this wave's LDS region
     //     (the phi(K) tile there is dead once the scores are formed)
-    bf16x8 vf[5];
+    bf16x8 vf[NMT];
 #pragma unroll
-    for (int mt = 0; mt < 5; ++mt) {
+    for (int mt = 0; mt < NMT; ++mt) {
       const int row = 16 * mt + c;
       vf[mt] = *(const bf16x8*)&vt[row * CROW + ((g ^ ((row >> 3) & 3)) << 3)];
     }
@@ -356,11 +361,11 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     __builtin_amdgcn_wave_barrier();
     // S_prev,w^T A fragments (bf16, the feature order of (c) and (e)), once
     // per chunk for both query halves
-    bf16x8 sa[KS][5];
+    bf16x8 sa[KS][NMT];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int mt = 0; mt < 5; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = acc_s[(KS == 2 ? 2 * s : 0) + (j & 1)][mt][j >> 1];
@@ -368,15 +373,15 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       }
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
-      floatx4 ao[5];
+      floatx4 ao[NMT];
 #pragma unroll
-      for (int mt = 0; mt < 5; ++mt) ao[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < NMT; ++mt) ao[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int mt = 0; mt < 5; ++mt) ao[mt] = mfma16(sa[s][mt], bq[s][nq], ao[mt]);
+        for (int mt = 0; mt < NMT; ++mt) ao[mt] = mfma16(sa[s][mt], bq[s][nq], ao[mt]);
 #pragma unroll
-      for (int mt = 0; mt < 5; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
         ao[mt] = mfma16(vf[mt], bs[nq], ao[mt]);
         *(floatx4*)&Red[w][((mt * 2 + nq) * 64 + lane) * 4] = ao[mt];
       }
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int n = 0; n < 5; ++n) acc_s[ft][n] = mfma16(fk[ft], vf[n], acc_s[ft][n]);
+      for (int n = 0; n < NMT; ++n) acc_s[ft][n] = mfma16(fk[ft], vf[n], acc_s[ft][n]);
   };
 
   // Sum the waves' partial out^T tiles (mt < 4) and normalise by row 64
