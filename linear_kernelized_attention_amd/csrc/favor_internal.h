@@ -90,10 +90,23 @@ size_t backward_workspace_bytes(const Problem& p);
 hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
                         PhaseHook* hook);
 size_t dphi_lds(const Problem& p);
+// Fragments the feature-gradient kernel copies into LDS: M as A fragments
+// [BH][F / 16][2][64][8] bf16, its z column [BH][F] float32, the (s Omega)^T
+// fragments [m / 32][4][64][8] and the ReLU residual fragments
+// [m / 16][2][64][8] (bf16).
+struct DphiPrep {
+  uint16_t* mfrag;
+  float* zsum;
+  uint16_t* otfrag;
+  uint16_t* olofrag;
+};
+DphiPrep dphi_prep_layout(const Problem& p, void* base, size_t* bytes);
+hipError_t launch_dphi_prep(const Problem& p, const uint16_t* part, long long stride, int nsum,
+                            const float* Omega, const DphiPrep& prep, bool with_omega,
+                            hipStream_t s);
 hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
-                       const float* Omega, const uint16_t* part, long long stride, int nsum,
-                       const uint16_t* Wv, const float* wz, uint16_t* DX, bool keys,
-                       hipStream_t s);
+                       const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                       bool keys, hipStream_t s);
 }  // namespace mfma
 
 namespace block {

@@ -16,11 +16,14 @@
 // forward state) and w = [a, b]; keys take M = R = sum_i u(q_i) [a_i, b_i]^T
 // and w = [v, 1].  Every dropped constant cancels between the two sides.
 //
-// One block of DPHI_NW waves handles 64 tokens per wave.  The prologue
-// sums the side's partial states and stores M in LDS as MFMA A fragments
-// with 8 consecutive value columns of one feature per lane (the transpose
-// of the readout's layout), next to the Omega~ fragments of the projection
-// and (s Omega)^T fragments whose row order matches the dP C fragments.
+// A prep kernel, once per head and side, sums the side's partial states
+// and writes M as MFMA A fragments with 8 consecutive value columns of one
+// feature per lane (the transpose of the readout's layout) and the z
+// column; once per call it also writes the (s Omega)^T fragments, whose row
+// order matches the dP C fragments, and (ReLU) the Omega residual
+// fragments.  One block of DPHI_NW waves handles 64 tokens per wave; its
+// prologue copies these fragments and the Omega~ fragments of the
+// projection into LDS with 16-byte loads.
 // Per Omega row pair and 16-token tile: the projection (4 MFMA), the
 // feature map, w^ (8 MFMA for trig, 4 otherwise, plus the rank-1 z term on
 // the VALU), dP, and dx^T += (s Omega)^T dP (4 MFMA) -- the C fragment of
@@ -45,12 +48,77 @@ constexpr size_t dphi_lds_bytes() {
          + (size_t)F * sizeof(float);                                    // z column of M
 }
 
+// Blocks [0, BH * F / 16): head bh, feature tile ft -- the sum of the nsum
+// partial states' rows 16 ft .. 16 ft + 15 as A fragments (ks, lane 16 g + c,
+// slot j: feature 16 ft + c, column 32 ks + 8 g + j) and their z values.
+// Remaining blocks (with_omega): the (s Omega)^T fragments (i, dt), lane
+// 16 g + c, slot j: s Omega[32 i + 16 (j / 4) + 4 g + j % 4][16 dt + c], and
+// (ReLU) the residual fragments (o, kk): Omega - bf16(Omega) at row
+// 16 o + c, column 32 kk + 8 g + j.
+__global__ __launch_bounds__(256) void dphi_prep_kernel(const uint16_t* __restrict__ part,
+                                                        long long split_stride, int nsum, int F,
+                                                        long long BH, const float* __restrict__ Omega,
+                                                        int m, int relu, float dx_scale,
+                                                        DphiPrep prep) {
+  const int NFT = F / 16;
+  const long long b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (b < BH * NFT) {
+    const long long bh = b / NFT;
+    const int ft = (int)(b % NFT);
+    __shared__ float t[16][65];   // [feature][column]
+    const uint16_t* pb = part + (size_t)bh * state_elems(F);
+    // state tile (ft, n), lane l' = tid % 64 of tile n = tid / 64: features
+    // 16 ft + 4 (l' / 16) + r, r = 0..3, of column 16 n + l' % 16 (8 bytes)
+    {
+      const int n = tid >> 6, l = tid & 63;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < nsum; ++sp) {
+        const u32x2 raw = *(const u32x2*)(pb + sp * split_stride + vtile_off(ft, n) + l * 4);
+        v[0] += __uint_as_float(raw[0] << 16);
+        v[1] += __uint_as_float(raw[0] & 0xffff0000u);
+        v[2] += __uint_as_float(raw[1] << 16);
+        v[3] += __uint_as_float(raw[1] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[4 * (l >> 4) + r][16 * n + (l & 15)] = v[r];
+    }
+    if (tid < 16) {
+      float z = 0.f;
+      for (int sp = 0; sp < nsum; ++sp) z += bf16_to_f32(pb[sp * split_stride + z_off(F, 16 * ft + tid)]);
+      prep.zsum[(size_t)bh * F + 16 * ft + tid] = z;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const int ks = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = t[c][32 * ks + 8 * g + j];
+      *(bf16x8*)(prep.mfrag + (((size_t)bh * NFT + ft) * 2 + ks) * 512 + l * 8) = pack8(v);
+    }
+    return;
+  }
+  const long long e0 = (b - BH * NFT) * 256 + tid;
+  const long long stride = ((long long)gridDim.x - BH * NFT) * 256;
+  const int npair = m / 32, nrt = m / 16;
+  for (long long e = e0; e < (long long)npair * 4 * 512; e += stride) {
+    const int j = (int)(e & 7), l = (int)((e >> 3) & 63), dt = (int)((e >> 9) & 3), i = (int)(e >> 11);
+    const int row = 32 * i + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3);
+    prep.otfrag[e] = bf16_bits(dx_scale * Omega[(size_t)row * D + 16 * dt + (l & 15)]);
+  }
+  if (relu)
+    for (long long e = e0; e < (long long)nrt * 2 * 512; e += stride) {
+      const int j = (int)(e & 7), l = (int)((e >> 3) & 63), kk = (int)((e >> 9) & 1), o = (int)(e >> 10);
+      const float x = Omega[(size_t)(16 * o + (l & 15)) * D + 32 * kk + 8 * (l >> 4) + j];
+      prep.olofrag[e] = bf16_bits(x - bf16_to_f32(bf16_bits(x)));
+    }
+}
+
 template <int KIND, int NPAIR>
 __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ ofrag,
-    const float* __restrict__ Omega, const uint16_t* __restrict__ part, long long split_stride,
-    int nsum, const uint16_t* __restrict__ Wv, const float* __restrict__ wz,
-    uint16_t* __restrict__ DX, int L, long long BH, int keys, float dx_scale) {
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ ofrag, DphiPrep prep,
+    const uint16_t* __restrict__ Wv, const float* __restrict__ wz,
+    uint16_t* __restrict__ DX, int L, long long BH, int keys) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr bool POS = KIND == KIND_POS;
   constexpr int M = 32 * NPAIR;
@@ -75,51 +143,17 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
   const long long t0 = (long long)blk * DPHI_NW * QW + (long long)w * QW;
   const size_t head = (size_t)bh * L * D;
 
-  // M (sum of nsum partial states) transposed into row fragments: state
-  // tile (ft, n) lane l' holds features 16 ft + 4 g' + r of column
-  // 16 n + c'; row fragment (ft, ks) lane 16 g + c slot j holds feature
-  // 16 ft + c, column 32 ks + 8 g + j.
-  const uint16_t* pb = part + (size_t)bh * state_elems(F);
-  for (int it = tid; it < NFT * 4 * 64; it += NT) {
-    const int ft = it >> 8, n = (it >> 6) & 3, lp = it & 63;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nsum; ++sp) {
-      const u32x2 raw = *(const u32x2*)(pb + sp * split_stride + vtile_off(ft, n) + lp * 4);
-      v[0] += __uint_as_float(raw[0] << 16);
-      v[1] += __uint_as_float(raw[0] & 0xffff0000u);
-      v[2] += __uint_as_float(raw[1] << 16);
-      v[3] += __uint_as_float(raw[1] & 0xffff0000u);
-    }
-    const int col = 16 * n + (lp & 15), ks = col >> 5, gg = (col & 31) >> 3, j = col & 7;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int cc = 4 * (lp >> 4) + r;
-      Mr[((ft * 2 + ks) * 64 + 16 * gg + cc) * 8 + j] = bf16_bits(v[r]);
-    }
+  // M row fragments and z (prepared per head), the Omega~ fragments, the
+  // (s Omega)^T fragments and (ReLU) the residual fragments: 16-byte copies
+  {
+    const u32x4* src = (const u32x4*)(prep.mfrag + (size_t)bh * NFT * 2 * 512);
+    for (int i = tid; i < NFT * 2 * 64; i += NT) ((u32x4*)Mr)[i] = src[i];
   }
-  for (int f = tid; f < F; f += NT) {
-    float z = 0.f;
-    for (int sp = 0; sp < nsum; ++sp) z += bf16_to_f32(pb[sp * split_stride + z_off(F, f)]);
-    zl[f] = z;
-  }
+  for (int f = tid; f < F; f += NT) zl[f] = prep.zsum[(size_t)bh * F + f];
   for (int i = tid; i < NOT * 2 * 64; i += NT) ((u32x4*)Ol)[i] = ((const u32x4*)ofrag)[i];
-  if (RELU) {
-    // residual fragment (o, kk), lane 16 g + c, slot j: Omega row 16 o + c,
-    // column 32 kk + 8 g + j (the ReLU projection is unscaled)
-    for (int e = tid; e < NOT * 2 * 512; e += NT) {
-      const int j = e & 7, l = (e >> 3) & 63, kk = (e >> 9) & 1, o = e >> 10;
-      const float x = Omega[(size_t)(16 * o + (l & 15)) * D + 32 * kk + 8 * (l >> 4) + j];
-      Olo[e] = bf16_bits(x - bf16_to_f32(bf16_bits(x)));
-    }
-  }
-  // (s Omega)^T fragment (i, dt), lane 16 g + c, slot j: Omega row
-  // 32 i + 16 (j / 4) + 4 g + j % 4 (the dP C fragment's order), column
-  // 16 dt + c
-  for (int e = tid; e < NPAIR * 4 * 512; e += NT) {
-    const int j = e & 7, l = (e >> 3) & 63, dt = (e >> 9) & 3, i = e >> 11;
-    const int row = 32 * i + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3);
-    Ot[e] = bf16_bits(dx_scale * Omega[(size_t)row * D + 16 * dt + (l & 15)]);
-  }
+  if (RELU)
+    for (int i = tid; i < NOT * 2 * 64; i += NT) ((u32x4*)Olo)[i] = ((const u32x4*)prep.olofrag)[i];
+  for (int i = tid; i < NPAIR * 4 * 64; i += NT) ((u32x4*)Ot)[i] = ((const u32x4*)prep.otfrag)[i];
   __syncthreads();
   if (t0 >= L) return;
 
@@ -176,6 +210,18 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         ot[dt] = *(const bf16x8*)(Ot + ((size_t)(i * 4 + dt) * 64 + lane) * 8);
+      // this pair's M row fragments and z values, shared by both token tiles
+      bf16x8 mf[NH][2][2];
+      floatx4 zf[NH][2];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int o2 = 0; o2 < 2; ++o2) {
+          const int ft = (h * M + 32 * i + 16 * o2) / 16;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) mf[h][o2][ks] = *(const bf16x8*)(Mr + ((size_t)(ft * 2 + ks) * 64 + lane) * 8);
+          zf[h][o2] = *(const floatx4*)&zl[16 * ft + 4 * g];
+        }
 #pragma unroll
       for (int n2 = 0; n2 < 2; ++n2) {
         floatx4 P[2];
@@ -197,13 +243,11 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
         for (int h = 0; h < NH; ++h)
 #pragma unroll
           for (int o2 = 0; o2 < 2; ++o2) {
-            const int ft = (h * M + 32 * i + 16 * o2) / 16;
             floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              a = mfma16(*(const bf16x8*)(Mr + ((size_t)(ft * 2 + ks) * 64 + lane) * 8), wf[n2][ks], a);
+            for (int ks = 0; ks < 2; ++ks) a = mfma16(mf[h][o2][ks], wf[n2][ks], a);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = fmaf(zl[16 * ft + 4 * g + r], wzv[n2], a[r]);
+            for (int r = 0; r < 4; ++r) a[r] = fmaf(zf[h][o2][r], wzv[n2], a[r]);
             wh[h][o2] = a;
           }
         float dP[2][4];
@@ -262,9 +306,8 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
 
 template <int KIND, int NPAIR>
 hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
-                         const float* Omega, const uint16_t* part, long long stride, int nsum,
-                         const uint16_t* Wv, const float* wz, uint16_t* DX, bool keys,
-                         hipStream_t s) {
+                         const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                         bool keys, hipStream_t s) {
   constexpr int M = 32 * NPAIR;
   constexpr int F = KIND == KIND_TRIG ? 2 * M : M;
   auto kern = dphi_kernel<KIND, NPAIR>;
@@ -274,28 +317,25 @@ hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* of
   }();
   (void)attr;
   const long long nb = (p.L + DPHI_NW * QW - 1) / (DPHI_NW * QW);
-  const float dx_scale = KIND == KIND_RELU ? 1.0f : powf((float)D, -0.25f);
   const size_t lds = dphi_lds_bytes<M, F, KIND == KIND_RELU>();
   hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(DPHI_NW * 64), lds, s,
-                     X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, p.L, p.BH, keys ? 1 : 0,
-                     dx_scale);
+                     X, ofrag, prep, Wv, wz, DX, p.L, p.BH, keys ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int KIND>
 hipError_t launch_dphi_k(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
-                         const float* Omega, const uint16_t* part, long long stride, int nsum,
-                         const uint16_t* Wv, const float* wz, uint16_t* DX, bool keys,
-                         hipStream_t s) {
+                         const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                         bool keys, hipStream_t s) {
   switch (p.m / 32) {
-    case 1: return launch_dphi_t<KIND, 1>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 2: return launch_dphi_t<KIND, 2>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 3: return launch_dphi_t<KIND, 3>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 4: return launch_dphi_t<KIND, 4>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 5: return launch_dphi_t<KIND, 5>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 6: return launch_dphi_t<KIND, 6>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    case 7: return launch_dphi_t<KIND, 7>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-    default: return launch_dphi_t<KIND, 8>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
+    case 1: return launch_dphi_t<KIND, 1>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 2: return launch_dphi_t<KIND, 2>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 3: return launch_dphi_t<KIND, 3>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 4: return launch_dphi_t<KIND, 4>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 5: return launch_dphi_t<KIND, 5>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 6: return launch_dphi_t<KIND, 6>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    case 7: return launch_dphi_t<KIND, 7>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    default: return launch_dphi_t<KIND, 8>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
   }
 }
 
@@ -306,15 +346,37 @@ size_t dphi_lds(const Problem& p) {
          (size_t)p.F * sizeof(float);
 }
 
+DphiPrep dphi_prep_layout(const Problem& p, void* base, size_t* bytes) {
+  DphiPrep d;
+  const size_t mf = align_up((size_t)p.BH * p.F * 64 * sizeof(uint16_t), 256);
+  const size_t zs = align_up((size_t)p.BH * p.F * sizeof(float), 256);
+  const size_t ot = align_up((size_t)(p.m / 32) * 4 * 512 * sizeof(uint16_t), 256);
+  const size_t lo = align_up((size_t)(p.m / 16) * 2 * 512 * sizeof(uint16_t), 256);
+  char* c = (char*)base;
+  d.mfrag = (uint16_t*)c;
+  d.zsum = (float*)(c + mf);
+  d.otfrag = (uint16_t*)(c + mf + zs);
+  d.olofrag = (uint16_t*)(c + mf + zs + ot);
+  *bytes = mf + zs + ot + lo;
+  return d;
+}
+
+hipError_t launch_dphi_prep(const Problem& p, const uint16_t* part, long long stride, int nsum,
+                            const float* Omega, const DphiPrep& prep, bool with_omega,
+                            hipStream_t s) {
+  const long long nb = p.BH * (p.F / 16) + (with_omega ? 64 : 0);
+  const float dx_scale = p.kind == KIND_RELU ? 1.0f : powf((float)D, -0.25f);
+  hipLaunchKernelGGL(dphi_prep_kernel, dim3((unsigned)nb), dim3(256), 0, s, part, stride, nsum, p.F,
+                     p.BH, Omega, p.m, p.kind == KIND_RELU ? 1 : 0, dx_scale, prep);
+  return hipGetLastError();
+}
+
 hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
-                       const float* Omega, const uint16_t* part, long long stride, int nsum,
-                       const uint16_t* Wv, const float* wz, uint16_t* DX, bool keys,
-                       hipStream_t s) {
-  if (p.kind == KIND_TRIG)
-    return launch_dphi_k<KIND_TRIG>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-  if (p.kind == KIND_POS)
-    return launch_dphi_k<KIND_POS>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
-  return launch_dphi_k<KIND_RELU>(p, X, ofrag, Omega, part, stride, nsum, Wv, wz, DX, keys, s);
+                       const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                       bool keys, hipStream_t s) {
+  if (p.kind == KIND_TRIG) return launch_dphi_k<KIND_TRIG>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+  if (p.kind == KIND_POS) return launch_dphi_k<KIND_POS>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+  return launch_dphi_k<KIND_RELU>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
 }
 
 }  // namespace mfma

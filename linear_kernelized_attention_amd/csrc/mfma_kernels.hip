@@ -501,7 +501,7 @@ bool lds_fits(const Problem& p) { return readout_lds(p) <= 160 * 1024; }
 // summed R.
 struct BwdLayout {
   Plan pl;
-  size_t red, ab, bh, total;
+  size_t red, ab, bh, prep, total;
 };
 
 BwdLayout bwd_layout(const Problem& p) {
@@ -510,7 +510,8 @@ BwdLayout bwd_layout(const Problem& p) {
   bl.red = red_bytes(p, bl.pl);
   bl.ab = align_up((size_t)p.BH * p.L * D * sizeof(uint16_t), 256);
   bl.bh = align_up((size_t)p.BH * p.L * sizeof(float), 256);
-  bl.total = 2 * (bl.pl.part_bytes + bl.red) + bl.pl.ofrag_bytes + bl.ab + bl.bh;
+  (void)dphi_prep_layout(p, nullptr, &bl.prep);
+  bl.total = 2 * (bl.pl.part_bytes + bl.red) + bl.pl.ofrag_bytes + bl.ab + bl.bh + bl.prep;
   return bl;
 }
 
@@ -528,6 +529,8 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   float* bhat = (float*)((char*)ab + bl.ab);
   uint16_t* partR = (uint16_t*)((char*)bhat + bl.bh);
   uint16_t* redR = (uint16_t*)((char*)partR + pl.part_bytes);
+  size_t prep_bytes;
+  const DphiPrep prep = dphi_prep_layout(p, (char*)redR + bl.red, &prep_bytes);
   const long long stride = (long long)split_stride_elems(p);
   const long long per8 = stride / 8;
   auto sum_splits = [&](const uint16_t* part, uint16_t* red, const uint16_t** src, int* nsum) {
@@ -568,13 +571,16 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   phase_end(hook, s);
   // dQ from (S, [a, b]); dK from (R, [v, 1]); dV = R^T u(k) (trig: times c_k)
   phase_begin(hook, s, "mfma_bwd_dq");
-  hipError_t e = launch_dphi(p, (const uint16_t*)b.q, ofrag, b.omega, srcS, stride, nS, ab, bhat,
-                             (uint16_t*)gb.dq, false, s);
+  hipError_t e = launch_dphi_prep(p, srcS, stride, nS, b.omega, prep, true, s);
+  if (e != hipSuccess) return e;
+  e = launch_dphi(p, (const uint16_t*)b.q, ofrag, prep, ab, bhat, (uint16_t*)gb.dq, false, s);
   phase_end(hook, s);
   if (e != hipSuccess) return e;
   phase_begin(hook, s, "mfma_bwd_dk");
-  e = launch_dphi(p, (const uint16_t*)b.k, ofrag, b.omega, srcR, stride, nR, (const uint16_t*)b.v,
-                  nullptr, (uint16_t*)gb.dk, true, s);
+  e = launch_dphi_prep(p, srcR, stride, nR, b.omega, prep, false, s);
+  if (e != hipSuccess) return e;
+  e = launch_dphi(p, (const uint16_t*)b.k, ofrag, prep, (const uint16_t*)b.v, nullptr,
+                  (uint16_t*)gb.dk, true, s);
   phase_end(hook, s);
   if (e != hipSuccess) return e;
   phase_begin(hook, s, "mfma_bwd_dv");
