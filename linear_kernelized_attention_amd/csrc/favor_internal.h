@@ -93,12 +93,15 @@ size_t dphi_lds(const Problem& p);
 // Fragments the feature-gradient kernel copies into LDS: M as A fragments
 // [BH][F / 16][2][64][8] bf16, its z column [BH][F] float32, the (s Omega)^T
 // fragments [m / 32][4][64][8] and the ReLU residual fragments
-// [m / 16][2][64][8] (bf16).
+// [m / 16][2][64][8] (bf16); and the same state as the readout's S^T
+// fragment image [BH][F / 32][5][64][8] bf16 (the readout copies it when
+// called with nsum = 0).
 struct DphiPrep {
   uint16_t* mfrag;
   float* zsum;
   uint16_t* otfrag;
   uint16_t* olofrag;
+  uint16_t* simg;
 };
 DphiPrep dphi_prep_layout(const Problem& p, void* base, size_t* bytes);
 hipError_t launch_dphi_prep(const Problem& p, const uint16_t* part, long long stride, int nsum,

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void dphi_prep_kernel(const uint16_t* __restri
     const long long bh = b / NFT;
     const int ft = (int)(b % NFT);
     __shared__ float t[16][65];   // [feature][column]
+    __shared__ float zs[16];
     const uint16_t* pb = part + (size_t)bh * state_elems(F);
     // state tile (ft, n), lane l' = tid % 64 of tile n = tid / 64: features
     // 16 ft + 4 (l' / 16) + r, r = 0..3, of column 16 n + l' % 16 (8 bytes)
@@ -87,8 +88,33 @@ __global__ __launch_bounds__(256) void dphi_prep_kernel(const uint16_t* __restri
       float z = 0.f;
       for (int sp = 0; sp < nsum; ++sp) z += bf16_to_f32(pb[sp * split_stride + z_off(F, 16 * ft + tid)]);
       prep.zsum[(size_t)bh * F + 16 * ft + tid] = z;
+      zs[tid] = z;
     }
     __syncthreads();
+    if (prep.simg) {
+      // the readout's S^T fragment image: fragment (ks, mt), lane l holds
+      // the C tiles of feature tiles 2 j and 2 j + 1 (slots 0..3, 4..7) at
+      // lane l, and for mt = 4 z[fbase + 4 (l / 16) ..] and
+      // z[fbase + 16 + 4 (l / 16) ..]; fbase = 16 * (ft & ~1), ks its
+      // k-step (trig: sin and cos k-steps interleaved)
+      const int fb = 16 * (ft & ~1), half = ft & 1;
+      int ks = fb / 32;
+      if (F == 2 * m) {
+        const int sg = fb >= m ? 1 : 0;
+        ks = 2 * ((fb - sg * m) / 32) + sg;
+      }
+      uint16_t* img = prep.simg + (size_t)bh * (F / 32) * 5 * 512;
+      for (int it = tid; it < 5 * 64; it += 256) {
+        const int mt = it >> 6, l = it & 63;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = mt < 4 ? t[4 * (l >> 4) + r][16 * mt + (l & 15)] : zs[4 * (l >> 4) + r];
+        u32x2 o;
+        o[0] = pack2(v[0], v[1]);
+        o[1] = pack2(v[2], v[3]);
+        *(u32x2*)(img + ((size_t)(ks * 5 + mt) * 64 + l) * 8 + 4 * half) = o;
+      }
+    }
     if (tid < 128) {
       const int ks = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
       float v[8];
@@ -352,12 +378,14 @@ DphiPrep dphi_prep_layout(const Problem& p, void* base, size_t* bytes) {
   const size_t zs = align_up((size_t)p.BH * p.F * sizeof(float), 256);
   const size_t ot = align_up((size_t)(p.m / 32) * 4 * 512 * sizeof(uint16_t), 256);
   const size_t lo = align_up((size_t)(p.m / 16) * 2 * 512 * sizeof(uint16_t), 256);
+  const size_t si = align_up((size_t)p.BH * (p.F / 32) * 5 * 512 * sizeof(uint16_t), 256);
   char* c = (char*)base;
   d.mfrag = (uint16_t*)c;
   d.zsum = (float*)(c + mf);
   d.otfrag = (uint16_t*)(c + mf + zs);
   d.olofrag = (uint16_t*)(c + mf + zs + ot);
-  *bytes = mf + zs + ot + lo;
+  d.simg = (uint16_t*)(c + mf + zs + ot + lo);
+  *bytes = mf + zs + ot + lo + si;
   return d;
 }
 

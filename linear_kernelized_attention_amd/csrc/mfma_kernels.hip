@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const uint16_t* __restri
 // fragment loads and the copy of the Omega~ A fragments (published by
 // kv_state), then sums the head's nsum partial states (at part + s *
 // split_stride) into S^T A fragments (bf16, all features; the fifth
-// fragment carries z in all 16 rows), all in LDS.  Then, per Omega row pair i (32 rows): projection
+// fragment carries z in all 16 rows), all in LDS; with nsum = 0, part is
+// that fragment image already summed (per head), and the prologue copies it.  Then, per Omega row pair i (32 rows): projection
 // P^T = Omega~ Q~^T for 4 token tiles, features (B fragments, features x
 // tokens), and the readout out^T += S^T phi^T.  The loop is fully unrolled
 // and software-pipelined: the feature map of pair i is independent of the
@@ -181,7 +182,11 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
       return z_off(F, fbase + 4 * (l >> 4));
     };
     const uint16_t* pb = part + (size_t)bh * state_elems(F);
-    if (nsum == 1) {
+    if (nsum == 0) {
+      // a prepared fragment image of this head's summed state
+      const u32x4* src = (const u32x4*)(part + (size_t)bh * NS * 8);
+      for (int i = tid; i < NS; i += NT) ((u32x4*)Sl)[i] = src[i];
+    } else if (nsum == 1) {
       constexpr int BATCH = 10;
       for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
         u32x2 v[BATCH][2];
@@ -553,12 +558,15 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   bk.ws = partS;
   launch_kv_nw<KIND>(p, bk, pl, ofrag, s, oscale);
   sum_splits(partS, redS, &srcS, &nS);
+  // S summed once per head into the fragments of the readout and of dphi
+  hipError_t e = launch_dphi_prep(p, srcS, stride, nS, b.omega, prep, true, s);
   phase_end(hook, s);
+  if (e != hipSuccess) return e;
   // a = g / den, b = -(g . num) / den^2 per query
   phase_begin(hook, s, "mfma_bwd_ab");
   Buffers bq = b;
   bq.out = ab;
-  launch_readout_m<KIND, RO_AB>(p, bq, srcS, stride, nS, ofrag, s, (const uint16_t*)gb.dout, bhat);
+  launch_readout_m<KIND, RO_AB>(p, bq, prep.simg, 0, 0, ofrag, s, (const uint16_t*)gb.dout, bhat);
   phase_end(hook, s);
   // R = sum_i u(q_i) [a_i, b_i]^T: the key-side kernel on (Q, a) with b in column 64
   phase_begin(hook, s, "mfma_bwd_rstate");
@@ -571,8 +579,6 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   phase_end(hook, s);
   // dQ from (S, [a, b]); dK from (R, [v, 1]); dV = R^T u(k) (trig: times c_k)
   phase_begin(hook, s, "mfma_bwd_dq");
-  hipError_t e = launch_dphi_prep(p, srcS, stride, nS, b.omega, prep, true, s);
-  if (e != hipSuccess) return e;
   e = launch_dphi(p, (const uint16_t*)b.q, ofrag, prep, ab, bhat, (uint16_t*)gb.dq, false, s);
   phase_end(hook, s);
   if (e != hipSuccess) return e;
@@ -587,7 +593,7 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   Buffers bv = b;
   bv.q = b.k;
   bv.out = gb.dv;
-  launch_readout_m<KIND, RO_DV>(p, bv, srcR, stride, nR, ofrag, s);
+  launch_readout_m<KIND, RO_DV>(p, bv, prep.simg, 0, 0, ofrag, s);
   phase_end(hook, s);
   return hipGetLastError();
 }
