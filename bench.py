@@ -280,6 +280,10 @@ def main():
     # instead of the throughput line: the estimator-quality sweep (error of
     # the GPU output against exact softmax over m and feature kinds)
     ap.add_argument("--estimator-sweep", action="store_true")
+    # instead of the throughput line: time one other workload alone (a
+    # forward workload name, "bwd_<workload>" for the backward pass, or
+    # "block"), e.g. to profile its kernels
+    ap.add_argument("--only", default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -299,6 +303,22 @@ def main():
     if args.estimator_sweep:
         from linear_kernelized_attention_amd import sweep
         print(json.dumps(sweep.run()), flush=True)
+        return
+    if args.only:
+        key = args.only
+        if key == "block":
+            sec = bench_block(F, I, args.steps, args.warmup)
+            rec = {"only": key, "us_per_call": sec * 1e6}
+        elif key.startswith("bwd_"):
+            wk = I.WORKLOADS[key[4:]]
+            sec = bench_backward(F, I, wk, args.steps, args.warmup)
+            rec = {"only": key, "us_per_call": sec * 1e6,
+                   "algorithmic_tflops": backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind) / sec / 1e12}
+        else:
+            wk = I.WORKLOADS[key]
+            sec, ph, rp = bench_attention(F, I, wk, args.steps, args.warmup, args.path)
+            rec = {"only": key, "us_per_call": sec * 1e6, "path": rp, "phases_ms": {n: t for n, t in ph}}
+        print(json.dumps(rec), flush=True)
         return
     if args.calibrate_copy:
         nbytes = calibrate_copy()
