@@ -28,6 +28,10 @@ SMALL = [
     # MFMA with Omega rows not a multiple of 128 (6 and 5 waves per key block)
     (1, 2, 200, 64, 96, "bf16"),
     (1, 1, 150, 64, 160, "bf16"),
+    # MFMA edge cases: one token; the fewest Omega rows (one wave per block); m = 128
+    (1, 2, 1, 64, 64, "bf16"),
+    (2, 1, 70, 64, 32, "bf16"),
+    (1, 1, 300, 64, 128, "bf16"),
 ]
 
 

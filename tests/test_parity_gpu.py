@@ -43,6 +43,8 @@ SMALL = [
     # MFMA with Omega rows not a multiple of 128 (6 and 5 waves per key block)
     (1, 2, 200, 64, 96, "bf16"),
     (1, 1, 150, 64, 160, "bf16"),
+    # the fewest Omega rows on MFMA (one wave per block)
+    (2, 1, 70, 64, 32, "bf16"),
 ]
 
 
