@@ -30,6 +30,12 @@ def test_every_declared_symbol_exported():
     assert set(names) == set(B.EXPORTS)
 
 
+def test_library_resolves_every_symbol_at_load():
+    # immediate binding: an internal function declared but left undefined
+    # would otherwise surface only at its first call
+    ctypes.CDLL(B.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_single_hip_runtime():
     F.lib()
     assert len(F.loaded_hip_runtimes()) <= 1
