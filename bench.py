@@ -158,9 +158,11 @@ def bench_block(F, I, steps, warmup):
     return time_calls(fn, steps, warmup)
 
 
-def bench_backward(F, I, w, steps, warmup):
+def bench_backward(F, I, w, steps, warmup, saved=False):
     """Seconds per favor_attention_backward call on a workload's seeded
-    inputs and a seeded N(0, 1) output gradient."""
+    inputs and a seeded N(0, 1) output gradient; with saved, the forward's
+    (out, den) from favor_attention(..., den=True), made once before timing,
+    is passed in (the training pattern)."""
     import torch
     ai, dr = I.workload_inputs(w)
     q, k, v = upload(ai, w.dtype)
@@ -171,8 +173,9 @@ def bench_backward(F, I, w, steps, warmup):
                                                       w.causal)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     grads = tuple(torch.empty_like(q) for _ in range(3))
+    sv = F.favor_attention(q, k, v, omega, kind=w.kind, causal=w.causal, den=True) if saved else None
     fn = lambda: F.favor_attention_backward(q, k, v, omega, g, kind=w.kind, causal=w.causal,
-                                            workspace=ws, grads=grads)
+                                            workspace=ws, grads=grads, saved=sv)
     return time_calls(fn, steps, warmup)
 
 
@@ -281,8 +284,9 @@ def main():
     # the GPU output against exact softmax over m and feature kinds)
     ap.add_argument("--estimator-sweep", action="store_true")
     # instead of the throughput line: time one other workload alone (a
-    # forward workload name, "bwd_<workload>" for the backward pass, or
-    # "block"), e.g. to profile its kernels
+    # forward workload name, "bwd_<workload>" for the backward pass,
+    # "bwds_<workload>" for it with the saved forward, or "block"), e.g. to
+    # profile its kernels
     ap.add_argument("--only", default=None)
     args = ap.parse_args()
 
@@ -309,9 +313,10 @@ def main():
         if key == "block":
             sec = bench_block(F, I, args.steps, args.warmup)
             rec = {"only": key, "us_per_call": sec * 1e6}
-        elif key.startswith("bwd_"):
-            wk = I.WORKLOADS[key[4:]]
-            sec = bench_backward(F, I, wk, args.steps, args.warmup)
+        elif key.startswith("bwd_") or key.startswith("bwds_"):
+            saved = key.startswith("bwds_")
+            wk = I.WORKLOADS[key.split("_", 1)[1]]
+            sec = bench_backward(F, I, wk, args.steps, args.warmup, saved)
             rec = {"only": key, "us_per_call": sec * 1e6,
                    "algorithmic_tflops": backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind) / sec / 1e12}
         else:
@@ -385,15 +390,17 @@ def main():
                           steps, 3)
         extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": cfg["B"] * cfg["L"] / sb,
                              "favor_us_per_call": sf * 1e6}
-        # backward pass on the headline, causal and B8 H8 L1024 shapes
-        for key in ("head", "c3_causal", "c2_trig"):
+        # backward pass on the headline, causal and B8 H8 L1024 shapes, and
+        # (bwds_) with the forward's saved output and row normalisers
+        for key, saved in (("head", False), ("c3_causal", False), ("c2_trig", False),
+                           ("head", True), ("c3_causal", True)):
             wk = I.WORKLOADS[key]
-            sbw = bench_backward(F, I, wk, max(5, steps // 10), 2)
+            sbw = bench_backward(F, I, wk, max(5, steps // 10), 2, saved)
             fl = backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind)
             rp = F.favor_attention_backward_resolve_path(wk.B, wk.H, wk.L, wk.d, wk.m, wk.dtype,
                                                          wk.kind, wk.causal)
             peak = PEAK_BF16_MFMA_TFLOPS if rp == "mfma" else PEAK_FP32_VALU_TFLOPS
-            extra[f"bwd_{key}"] = {"us_per_call": sbw * 1e6, "tokens_x_heads_per_s": wk.tokens_x_heads / sbw,
+            extra[f"{'bwds' if saved else 'bwd'}_{key}"] = {"us_per_call": sbw * 1e6, "tokens_x_heads_per_s": wk.tokens_x_heads / sbw,
                                    "path": rp, "algorithmic_tflops": fl / sbw / 1e12,
                                    "peak_frac": fl / sbw / 1e12 / peak,
                                    "peak": "bf16 MFMA" if rp == "mfma" else "fp32 VALU"}

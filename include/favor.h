@@ -135,6 +135,22 @@ int favor_attention_ex(const void* Q, const void* K, const void* V, const float*
                        int B, int H, int L, int d, int m, int dtype, int kind, int causal,
                        void* workspace, size_t workspace_bytes, void* stream, int path);
 
+/*
+ * favor_attention_train: favor_attention_ex that also writes the row
+ * normaliser of the output, den[b, h, i] = D_ii = phi(q_i) . sum_j phi(k_j)
+ * (j <= i when causal) with the full feature maps -- the diagonal of D in
+ * D^-1 A V (FAVOR+ blog page, section 核心机制：FAVOR+).  Kept with `out`,
+ * it lets favor_attention_backward_saved skip recomputing the forward.
+ *   den: float32 [B, H, L] device memory, 4-byte aligned, written; it must
+ *   not overlap any other argument (FAVOR_ERR_ALIAS).  Everything else as
+ *   favor_attention_ex (same workspace size).  The trig map's causal MFMA
+ *   path adds one small elementwise launch for den.
+ */
+int favor_attention_train(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                          float* den, int B, int H, int L, int d, int m, int dtype, int kind,
+                          int causal, void* workspace, size_t workspace_bytes, void* stream,
+                          int path);
+
 /* The favor_path that favor_attention_ex(..., path) would run (GENERIC or
  * MFMA), or a negative favor_status if the request is invalid/unsupported. */
 int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, int kind,
@@ -200,6 +216,21 @@ int favor_attention_backward(const void* Q, const void* K, const void* V, const 
                              const void* dOut, void* dQ, void* dK, void* dV, int B, int H, int L,
                              int d, int m, int dtype, int kind, int causal, void* workspace,
                              size_t workspace_bytes, void* stream);
+/*
+ * favor_attention_backward_saved: favor_attention_backward_ex given the
+ * forward's saved `out` and `den` (from favor_attention_train with the same
+ * inputs).  The MFMA family then forms a_i = dOut_i / den_i and
+ * b_i = -(dOut_i . out_i) / den_i in one elementwise pass instead of
+ * recomputing the forward's readout; the generic family recomputes and
+ * ignores them.  out: [B, H, L, d] dtype; den: float32 [B, H, L]; both
+ * read only, must not overlap the gradients or the workspace.  Same
+ * workspace size as favor_attention_backward_ex.
+ */
+int favor_attention_backward_saved(const void* Q, const void* K, const void* V,
+                                   const float* Omega, const void* out, const float* den,
+                                   const void* dOut, void* dQ, void* dK, void* dV, int B, int H,
+                                   int L, int d, int m, int dtype, int kind, int causal,
+                                   void* workspace, size_t workspace_bytes, void* stream, int path);
 int favor_attention_backward_ex(const void* Q, const void* K, const void* V, const float* Omega,
                                 const void* dOut, void* dQ, void* dK, void* dV, int B, int H,
                                 int L, int d, int m, int dtype, int kind, int causal,

@@ -34,6 +34,7 @@ EXPORTS = (
     "favor_attention", "favor_attention_ex", "favor_attention_resolve_path",
     "favor_profile_attention", "favor_embed_bf16", "favor_linear_bf16",
     "favor_pack_weight_bf16", "favor_embed_linear_bf16",
+    "favor_attention_train", "favor_attention_backward_saved",
     "favor_attention_backward_workspace_bytes", "favor_attention_backward",
     "favor_attention_backward_workspace_bytes_ex", "favor_attention_backward_ex",
 )
@@ -70,6 +71,8 @@ def _declare(lib: ctypes.CDLL) -> None:
         "favor_attention_backward": (i, [p] * 8 + [i] * 8 + [p, z, p]),
         "favor_attention_backward_workspace_bytes_ex": (z, [i] * 9),
         "favor_attention_backward_ex": (i, [p] * 8 + [i] * 8 + [p, z, p, i]),
+        "favor_attention_train": (i, [p] * 6 + [i] * 8 + [p, z, p, i]),
+        "favor_attention_backward_saved": (i, [p] * 10 + [i] * 8 + [p, z, p, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -196,11 +199,23 @@ def _call_args(q, k, v, omega, kind, causal, path, out, workspace):
 
 
 def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, path: str = "auto",
-                    out=None, workspace=None):
-    """FAVOR attention of [B, H, L, d] float32/bf16 tensors on the GPU."""
+                    out=None, workspace=None, den=None):
+    """FAVOR attention of [B, H, L, d] float32/bf16 tensors on the GPU.
+
+    With den (a float32 [B, H, L] tensor, or True to allocate one) the row
+    normalisers D_ii are written too, and (out, den) is returned: the pair
+    favor_attention_backward(..., saved=(out, den)) reuses."""
+    import torch
     args, out, _ = _call_args(q, k, v, omega, kind, causal, path, out, workspace)
-    _check(lib().favor_attention_ex(*args), "favor_attention")
-    return out
+    if den is None or den is False:
+        _check(lib().favor_attention_ex(*args), "favor_attention")
+        return out
+    if den is True:
+        den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if den.dtype != torch.float32 or tuple(den.shape) != tuple(q.shape[:3]) or not den.is_contiguous():
+        raise ValueError("den must be a contiguous float32 [B, H, L] tensor")
+    _check(lib().favor_attention_train(*args[:5], den.data_ptr(), *args[5:]), "favor_attention_train")
+    return out, den
 
 
 def favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="trig",
@@ -210,9 +225,10 @@ def favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="
 
 
 def favor_attention_backward(q, k, v, omega, dout, kind: str = "trig", causal: bool = False,
-                             path: str = "auto", workspace=None, grads=None):
+                             path: str = "auto", workspace=None, grads=None, saved=None):
     """(dq, dk, dv) of sum(dout * favor_attention(q, k, v)) on the GPU; grads
-    may supply the three output tensors."""
+    may supply the three output tensors; saved = (out, den) from
+    favor_attention(..., den=True) skips recomputing the forward (MFMA)."""
     import torch
     _validate(q, k, v, omega)
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
@@ -230,11 +246,20 @@ def favor_attention_backward(q, k, v, omega, dout, kind: str = "trig", causal: b
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads
-    _check(lib().favor_attention_backward_ex(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(), dout.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, m, dt, KIND[kind],
-        int(bool(causal)), workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device),
-        PATH[path]), "favor_attention_backward")
+    tail = [dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, m, dt,
+            KIND[kind], int(bool(causal)), workspace.data_ptr(), workspace.numel(),
+            _stream_ptr(q.device), PATH[path]]
+    head = [q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr()]
+    if saved is None:
+        _check(lib().favor_attention_backward_ex(*head, *tail), "favor_attention_backward")
+    else:
+        out, den = saved
+        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("saved out must be a contiguous tensor like q")
+        if den.dtype != torch.float32 or tuple(den.shape) != tuple(q.shape[:3]) or not den.is_contiguous():
+            raise ValueError("saved den must be a contiguous float32 [B, H, L] tensor")
+        _check(lib().favor_attention_backward_saved(*head, out.data_ptr(), den.data_ptr(), *tail),
+               "favor_attention_backward_saved")
     return dq, dk, dv
 
 

@@ -110,8 +110,9 @@ int check_call(const void* Q, const void* K, const void* V, const float* Omega, 
 }
 
 int launch(const Checked& c, const void* Q, const void* K, const void* V, const float* Omega,
-           void* out, void* ws, size_t wsb, hipStream_t s, favor::PhaseHook* hook) {
-  favor::Buffers b{Q, K, V, Omega, out, ws, wsb};
+           void* out, void* ws, size_t wsb, hipStream_t s, favor::PhaseHook* hook,
+           float* den = nullptr) {
+  favor::Buffers b{Q, K, V, Omega, out, ws, wsb, den};
   hipError_t e = c.path == FAVOR_PATH_MFMA ? favor::mfma::run(c.p, b, s, hook)
                                            : favor::generic::run(c.p, b, s, hook);
   if (e != hipSuccess) return FAVOR_ERR_HIP;
@@ -264,6 +265,28 @@ int favor_attention_ex(const void* Q, const void* K, const void* V, const float*
   return launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
 }
 
+int favor_attention_train(const void* Q, const void* K, const void* V, const float* Omega, void* out,
+                          float* den, int B, int H, int L, int d, int m, int dtype, int kind,
+                          int causal, void* workspace, size_t workspace_bytes, void* stream,
+                          int path) {
+  Checked c;
+  int st = check_call(Q, K, V, Omega, out, B, H, L, d, m, dtype, kind, causal, workspace,
+                      workspace_bytes, path, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  if (!den || ((uintptr_t)den & 3)) return FAVOR_ERR_INVALID_ARG;
+  const size_t esz = dtype == FAVOR_DTYPE_F32 ? 4 : 2;
+  const size_t tensor = (size_t)c.p.BH * (size_t)L * (size_t)d * esz;
+  const size_t denb = (size_t)c.p.BH * (size_t)L * sizeof(float);
+  const size_t need = ws_bytes(c.p, c.path);
+  if (overlaps(den, denb, Q, tensor) || overlaps(den, denb, K, tensor) ||
+      overlaps(den, denb, V, tensor) || overlaps(den, denb, out, tensor) ||
+      overlaps(den, denb, Omega, (size_t)m * d * sizeof(float)) ||
+      (need > 0 && overlaps(den, denb, workspace, need)))
+    return FAVOR_ERR_ALIAS;
+  return launch(c, Q, K, V, Omega, out, workspace, workspace_bytes, (hipStream_t)stream, nullptr,
+                den);
+}
+
 int favor_attention(const void* Q, const void* K, const void* V, const float* Omega, void* out,
                     int B, int H, int L, int d, int m, int dtype, int kind, int causal,
                     void* workspace, size_t workspace_bytes, void* stream) {
@@ -402,6 +425,38 @@ int favor_attention_backward_ex(const void* Q, const void* K, const void* V, con
   if (st != FAVOR_OK || c.empty) return st;
   favor::Buffers b{Q, K, V, Omega, nullptr, workspace, workspace_bytes};
   favor::BwdBuffers g{dOut, dQ, dK, dV};
+  const hipError_t e = c.path == FAVOR_PATH_MFMA
+                           ? favor::mfma::run_backward(c.p, b, g, (hipStream_t)stream, nullptr)
+                           : favor::generic::run_backward(c.p, b, g, (hipStream_t)stream, nullptr);
+  if (e != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipPeekAtLastError() != hipSuccess) {
+    (void)hipGetLastError();
+    return FAVOR_ERR_HIP;
+  }
+  return FAVOR_OK;
+}
+
+int favor_attention_backward_saved(const void* Q, const void* K, const void* V,
+                                   const float* Omega, const void* out, const float* den,
+                                   const void* dOut, void* dQ, void* dK, void* dV, int B, int H,
+                                   int L, int d, int m, int dtype, int kind, int causal,
+                                   void* workspace, size_t workspace_bytes, void* stream, int path) {
+  Checked c;
+  int st = check_backward(Q, K, V, Omega, dOut, dQ, dK, dV, B, H, L, d, m, dtype, kind, causal,
+                          workspace, workspace_bytes, path, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  if (!out || !den || !aligned16(out) || ((uintptr_t)den & 3)) return FAVOR_ERR_INVALID_ARG;
+  const size_t esz = dtype == FAVOR_DTYPE_F32 ? 4 : 2;
+  const size_t tensor = (size_t)c.p.BH * (size_t)L * (size_t)d * esz;
+  const size_t denb = (size_t)c.p.BH * (size_t)L * sizeof(float);
+  const size_t need = bwd_ws_bytes(c.p, c.path);
+  void* outs[] = {dQ, dK, dV};
+  for (void* o : outs)
+    if (overlaps(o, tensor, out, tensor) || overlaps(o, tensor, den, denb)) return FAVOR_ERR_ALIAS;
+  if (need > 0 && (overlaps(workspace, need, out, tensor) || overlaps(workspace, need, den, denb)))
+    return FAVOR_ERR_ALIAS;
+  favor::Buffers b{Q, K, V, Omega, nullptr, workspace, workspace_bytes};
+  favor::BwdBuffers g{dOut, dQ, dK, dV, out, den};
   const hipError_t e = c.path == FAVOR_PATH_MFMA
                            ? favor::mfma::run_backward(c.p, b, g, (hipStream_t)stream, nullptr)
                            : favor::generic::run_backward(c.p, b, g, (hipStream_t)stream, nullptr);

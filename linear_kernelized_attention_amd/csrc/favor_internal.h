@@ -26,6 +26,9 @@ struct Buffers {
   void* out;
   void* ws;
   size_t ws_bytes;
+  // optional forward output: the row normaliser D_ii = phi(q_i) . sum_j
+  // phi(k_j) (j <= i when causal), float32 [B, H, L], in the pages' units
+  float* den = nullptr;
 };
 
 // Optional per-kernel event recording (used by favor_profile_attention).
@@ -63,12 +66,16 @@ inline void phase_end(PhaseHook* h, hipStream_t s, int reps = 1) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Gradient buffers of the backward pass (device pointers, the input dtype).
+// Gradient buffers of the backward pass (device pointers, the input dtype);
+// optionally the forward's saved output and row normalisers (Buffers::den),
+// from which the MFMA family forms a and b without recomputing the forward.
 struct BwdBuffers {
   const void* dout;
   void* dq;
   void* dk;
   void* dv;
+  const void* out = nullptr;
+  const float* den = nullptr;
 };
 
 namespace generic {
@@ -110,6 +117,12 @@ hipError_t launch_dphi_prep(const Problem& p, const uint16_t* part, long long st
 hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
                        const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
                        bool keys, hipStream_t s);
+// a = dOut / den', b = -(dOut . out) / den' per token from the saved
+// forward (den' the device denominator: the row normaliser over the map's
+// scale), into a (bf16 [BH][L][64]) and b (float32 [BH][L]).
+hipError_t launch_saved_ab(const Problem& p, const uint16_t* Q, const uint16_t* G,
+                           const uint16_t* out, const float* den, uint16_t* ab, float* bhat,
+                           hipStream_t s);
 }  // namespace mfma
 
 namespace block {

@@ -47,6 +47,7 @@ struct Args {
   void* out;
   float* part;   // [n_seg][BH][F][d+1]
   float* total;  // [BH][F][d+1]
+  float* den;    // optional: the row normalisers [BH][L]
   long long BH;
   int L, d, m, kind, seg_len, n_seg;
 };
@@ -336,6 +337,7 @@ __global__ __launch_bounds__(NT) void readout_kernel(Args a, int causal) {
       if (e < TILE * dp1 && e % dp1 == d) den[e / dp1] = o[j];
     }
     __syncthreads();
+    if (a.den && tid < TILE && t0 + tid < t_end) a.den[(size_t)bh * a.L + t0 + tid] = den[tid];
 #pragma unroll
     for (int j = 0; j < ENT_O; ++j) {
       const int e = tid + j * NT;
@@ -385,6 +387,7 @@ hipError_t run_typed(const Problem& p, const Buffers& b, hipStream_t s, PhaseHoo
   a.part = (float*)b.ws;
   a.total = p.causal ? nullptr : (float*)((char*)b.ws + pl.part_bytes);
   a.BH = p.BH; a.L = p.L; a.d = p.d; a.m = p.m; a.kind = p.kind;
+  a.den = b.den;
   a.seg_len = pl.seg_len; a.n_seg = pl.n_seg;
   const long long n = p.BH * (long long)p.F * (p.d + 1);
 
@@ -953,6 +956,7 @@ hipError_t run_backward_typed(const Problem& p, const Buffers& b, const BwdBuffe
   ws += bp.rpart_bytes;
   ba.rtotal = p.causal ? nullptr : (float*)ws;
   a.BH = p.BH; a.L = p.L; a.d = p.d; a.m = p.m; a.kind = p.kind;
+  a.den = nullptr;
   a.seg_len = pl.seg_len; a.n_seg = pl.n_seg;
   ba.g = g.dout; ba.dq = g.dq; ba.dk = g.dk; ba.dv = g.dv;
   const long long n = p.BH * (long long)p.F * (p.d + 1);

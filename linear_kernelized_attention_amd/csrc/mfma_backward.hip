@@ -399,6 +399,57 @@ hipError_t launch_dphi_prep(const Problem& p, const uint16_t* part, long long st
   return hipGetLastError();
 }
 
+namespace {
+// One thread per (token, 8 columns); the 8 threads of a token reduce with
+// DPP.  den' = den / scale(q): scale = m^-1 (positive), m^-1 d^-1/2 (ReLU),
+// m^-1 exp(|q~|^2 / 2) (trig) -- the constants the device kernels drop.
+__global__ __launch_bounds__(256) void saved_ab_kernel(const uint16_t* __restrict__ Q,
+                                                       const uint16_t* __restrict__ G,
+                                                       const uint16_t* __restrict__ O,
+                                                       const float* __restrict__ den,
+                                                       uint16_t* __restrict__ ab,
+                                                       float* __restrict__ bhat, long long n_tok,
+                                                       int trig, float base_scale) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long t = i >> 3;
+  const int c8 = (int)(i & 7);
+  // threads past the last token take the last token (in bounds) so that
+  // every lane of an octet joins the reductions; they store nothing
+  const long long tc = min(t, n_tok - 1);
+  const size_t off = (size_t)tc * D + 8 * c8;
+  const bf16x8 g = *(const bf16x8*)(G + off);
+  const bf16x8 o = *(const bf16x8*)(O + off);
+  float go = 0.f, ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) go = fmaf((float)g[j], (float)o[j], go);
+  if (trig) {
+    const bf16x8 q = *(const bf16x8*)(Q + off);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf((float)q[j], (float)q[j], ss);
+  }
+  go = octet_sum(go);
+  ss = octet_sum(ss);
+  const float scale = trig ? base_scale * __expf(0.5f * ss * (1.0f / 8.0f)) : base_scale;
+  const float inv = scale / den[tc];   // 1 / den'
+  if (t >= n_tok) return;
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (float)g[j] * inv;
+  *(bf16x8*)(ab + off) = pack8(a);
+  if (c8 == 0) bhat[t] = -go * inv;
+}
+}  // namespace
+
+hipError_t launch_saved_ab(const Problem& p, const uint16_t* Q, const uint16_t* G,
+                           const uint16_t* out, const float* den, uint16_t* ab, float* bhat,
+                           hipStream_t s) {
+  const long long n_tok = p.BH * (long long)p.L;
+  const float base = p.kind == KIND_RELU ? 1.0f / (p.m * sqrtf((float)D)) : 1.0f / p.m;
+  hipLaunchKernelGGL(saved_ab_kernel, dim3((unsigned)((n_tok * 8 + 255) / 256)), dim3(256), 0, s, Q, G,
+                     out, den, ab, bhat, n_tok, p.kind == KIND_TRIG ? 1 : 0, base);
+  return hipGetLastError();
+}
+
 hipError_t launch_dphi(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
                        const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
                        bool keys, hipStream_t s) {

@@ -411,6 +411,12 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       float mul;
       if (MODE == C_DV) mul = TRIG ? __builtin_amdgcn_exp2f(Hq[buf][16 * nq + c]) : 1.f;
       else mul = 1.0f / den;
+      if (MODE == C_OUT && bhat && mt == 0 && g == 0 && valid) {
+        // optional output: the row normaliser in the pages' units -- the
+        // denominator times m^-1 (ReLU: also d^-1/2); the trig query weight
+        // exp(|q~|^2 / 2) is applied afterwards (den_trig_weight_kernel)
+        bhat[(size_t)bh * L + tok] = den * (TRIG || POS ? 1.0f / M : 1.0f / (8.0f * M));
+      }
       if (MODE == C_AB) {
         // a = G / den; the tile's 16 columns of G . num, over the lane groups
         const u32x2 raw = *(const u32x2*)(G + off);
@@ -467,6 +473,22 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     __syncthreads();
     store_b(t0);
   }
+}
+
+// den[t] *= exp(|q~_t|^2 / 2) for every token (the trig query weight of
+// the row normaliser); one thread per token row.
+__global__ __launch_bounds__(256) void den_trig_weight_kernel(const uint16_t* __restrict__ Q,
+                                                              float* __restrict__ den, long long n_tok) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_tok) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < D / 8; ++ch) {
+    const bf16x8 x = *(const bf16x8*)(Q + (size_t)t * D + 8 * ch);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf((float)x[j], (float)x[j], ss);
+  }
+  den[t] *= __expf(0.5f * ss * (1.0f / 8.0f));
 }
 
 // ---------------------------------------------------------------- host
@@ -533,8 +555,13 @@ hipError_t run_causal_kind(const Problem& p, const Buffers& b, hipStream_t s, Ph
   phase_end(hook, s, reps);
 
   phase_begin(hook, s, "mfma_causal_chunks");
-  for (int r = 0; r < reps; ++r) launch_causal_m<KIND>(p, b, cp, start, s, oscale);
+  for (int r = 0; r < reps; ++r) launch_causal_m<KIND>(p, b, cp, start, s, oscale, nullptr, b.den);
   phase_end(hook, s, reps);
+  if (KIND == KIND_TRIG && b.den) {
+    const long long n_tok = p.BH * (long long)p.L;
+    hipLaunchKernelGGL(den_trig_weight_kernel, dim3((unsigned)((n_tok + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)b.q, b.den, n_tok);
+  }
   return hipGetLastError();
 }
 
@@ -582,11 +609,18 @@ hipError_t run_causal_backward_kind(const Problem& p, const Buffers& b, const Bw
   launch_kv_nw<KIND>(p, bk, cp.keys, nullptr, s, oscale);
   launch_scan(p, cp, partS, startS, false, s);
   phase_end(hook, s);
-  // a = g / den, b = -(g . num) / den^2 per query
+  // a = g / den, b = -(g . num) / den^2 per query: from the saved forward
+  // when the caller has it, else from the recomputed causal forward
   phase_begin(hook, s, "mfma_bwd_ab");
-  Buffers bq = b;
-  bq.out = ab;
-  launch_causal_m<KIND, C_AB>(p, bq, cp, startS, s, oscale, (const uint16_t*)gb.dout, bhat);
+  if (gb.out && gb.den) {
+    const hipError_t e = launch_saved_ab(p, (const uint16_t*)b.q, (const uint16_t*)gb.dout,
+                                         (const uint16_t*)gb.out, gb.den, ab, bhat, s);
+    if (e != hipSuccess) return e;
+  } else {
+    Buffers bq = b;
+    bq.out = ab;
+    launch_causal_m<KIND, C_AB>(p, bq, cp, startS, s, oscale, (const uint16_t*)gb.dout, bhat);
+  }
   phase_end(hook, s);
   // R by segment (the key-side kernel on (Q, a) with b in column 64), and
   // its suffix over segments

@@ -352,6 +352,26 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
   for (int nt = 0; nt < 4; ++nt) {
     float mul = 1.0f / acc[4][nt][0];
     if (MODE == RO_DV) mul = TRIG ? __builtin_amdgcn_exp2f(hq[nt]) : 1.0f;
+    if (MODE == RO_OUT && bhat) {
+      // optional output: the row normaliser in the pages' units, the device
+      // denominator times m^-1 (the two m^-1/2 factors), d^-1/2 (ReLU's
+      // unscaled projection) or the trig query weight exp(|q~|^2 / 2)
+      float scale = TRIG || POS ? 1.0f / M : 1.0f / (8.0f * M);
+      if (TRIG) {
+        const long long tok = min(t0 + 16 * nt + c, (long long)L - 1);
+        float ss = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 x = *(const bf16x8*)(Q + head + (size_t)tok * D + 32 * kk + 8 * g);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fmaf((float)x[j], (float)x[j], ss);
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        scale *= __expf(0.5f * ss * (1.0f / 8.0f));
+      }
+      if (g == 0 && t0 + 16 * nt + c < L) bhat[(size_t)bh * L + t0 + 16 * nt + c] = acc[4][nt][0] * scale;
+    }
     if (MODE == RO_AB) {
       // b = -(g . num) / den^2: this lane's 16 columns, then the 4 lane groups
       const long long tok = min(t0 + 16 * nt + c, (long long)L - 1);
@@ -493,7 +513,7 @@ hipError_t run_kind(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook
   }
 
   phase_begin(hook, s, "mfma_readout");
-  for (int r = 0; r < reps; ++r) launch_readout_m<KIND>(p, b, src, stride, nsum, ofrag, s);
+  for (int r = 0; r < reps; ++r) launch_readout_m<KIND>(p, b, src, stride, nsum, ofrag, s, nullptr, b.den);
   phase_end(hook, s, reps);
   return hipGetLastError();
 }
@@ -562,11 +582,18 @@ hipError_t run_backward_kind(const Problem& p, const Buffers& b, const BwdBuffer
   hipError_t e = launch_dphi_prep(p, srcS, stride, nS, b.omega, prep, true, s);
   phase_end(hook, s);
   if (e != hipSuccess) return e;
-  // a = g / den, b = -(g . num) / den^2 per query
+  // a = g / den, b = -(g . num) / den^2 per query: from the saved forward
+  // when the caller has it, else from a readout of S
   phase_begin(hook, s, "mfma_bwd_ab");
-  Buffers bq = b;
-  bq.out = ab;
-  launch_readout_m<KIND, RO_AB>(p, bq, prep.simg, 0, 0, ofrag, s, (const uint16_t*)gb.dout, bhat);
+  if (gb.out && gb.den) {
+    e = launch_saved_ab(p, (const uint16_t*)b.q, (const uint16_t*)gb.dout, (const uint16_t*)gb.out,
+                        gb.den, ab, bhat, s);
+    if (e != hipSuccess) return e;
+  } else {
+    Buffers bq = b;
+    bq.out = ab;
+    launch_readout_m<KIND, RO_AB>(p, bq, prep.simg, 0, 0, ofrag, s, (const uint16_t*)gb.dout, bhat);
+  }
   phase_end(hook, s);
   // R = sum_i u(q_i) [a_i, b_i]^T: the key-side kernel on (Q, a) with b in column 64
   phase_begin(hook, s, "mfma_bwd_rstate");

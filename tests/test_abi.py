@@ -196,6 +196,38 @@ def test_backward_alias_checks():
     assert bcall(ws=DQA) == B.FAVOR_ERR_ALIAS         # workspace over an output
 
 
+# saved-forward entry points: den [B, H, L] float32 and the saved output;
+# the backward's workspace sits above every other fake buffer
+DENA, SOA, BWS = 0x100000 * 11, 0x100000 * 12, 0x100000 * 64
+
+
+def tcall(den=DENA, o=OA, q=QA, ws=WS, L=64, path=0):
+    return F.lib().favor_attention_train(q, KA, VA, WA, o, den, 2, 2, L, 64, 256, 1, 0, 0, ws,
+                                         1 << 30, None, path)
+
+
+def scall(out=SOA, den=DENA, dq=DQA, ws=BWS, L=64):
+    return F.lib().favor_attention_backward_saved(QA, KA, VA, WA, out, den, GA, dq, DKA, DVA, 2, 2,
+                                                  L, 64, 256, 1, 0, 0, ws, 1 << 40, None, 0)
+
+
+def test_saved_forward_argument_checks():
+    assert tcall(den=0) == B.FAVOR_ERR_INVALID_ARG
+    assert tcall(den=DENA + 2) == B.FAVOR_ERR_INVALID_ARG     # misaligned
+    assert tcall(den=OA + 16) == B.FAVOR_ERR_ALIAS            # over the output
+    assert tcall(den=QA) == B.FAVOR_ERR_ALIAS                 # over an input
+    assert tcall(den=WS + 64) == B.FAVOR_ERR_ALIAS            # over the workspace
+    assert tcall(path=9) == B.FAVOR_ERR_INVALID_ARG
+    assert tcall(den=0, o=0, q=0, ws=0, L=0) == B.FAVOR_OK     # empty: nothing touched
+    assert scall(out=0) == B.FAVOR_ERR_INVALID_ARG
+    assert scall(den=0) == B.FAVOR_ERR_INVALID_ARG
+    assert scall(out=SOA + 8) == B.FAVOR_ERR_INVALID_ARG      # misaligned
+    assert scall(dq=SOA) == B.FAVOR_ERR_ALIAS                 # gradient over the saved output
+    assert scall(dq=DENA) == B.FAVOR_ERR_ALIAS                # gradient over den
+    assert scall(ws=DENA) == B.FAVOR_ERR_ALIAS                # workspace over den
+    assert scall(L=0, out=0, den=0) == B.FAVOR_OK
+
+
 def test_backward_workspace_covers_forward_state():
     shape = (1, 8, 4096, 64, 256, "bf16", "trig")
     for causal in (False, True):
