@@ -11,3 +11,4 @@ from ._lib import (  # noqa: F401
     favor_pack_weight_bf16, favor_embed_linear_bf16, favor_block_weights, BlockWeights,
     favor_performer_block, favor_profile_attention, lib, loaded_hip_runtimes, status_string,
 )
+from .autograd import FavorAttentionFunction, favor_attention_fn  # noqa: F401,E402

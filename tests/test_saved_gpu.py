@@ -107,3 +107,25 @@ def test_backward_saved(shape, kind, causal):
               + " ".join(f"{e:.2e}" for e in errs), flush=True)
         for name, e in zip(("dq", "dk", "dv"), errs):
             assert e <= TOL[dtype], (path, name, e)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_function(causal):
+    # loss.backward() through the autograd wrapper gives the gradients of the
+    # direct backward call, and the forward gives favor_attention's output
+    shape = (2, 2, 200, 64, 64, "bf16")
+    B, H, L, d, m, dtype = shape
+    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=5)
+    gs, _ = I.output_grads(B, H, L, d, dtype, seed=5)
+    g_dev = to_device(gs, dtype)
+    leaves = [x.clone().requires_grad_(True) for x in dev[:3]]
+    out = F.favor_attention_fn(*leaves, dev[3], kind="trig", causal=causal)
+    out.backward(g_dev)
+    want_out = F.favor_attention(*dev, kind="trig", causal=causal)
+    want = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().view(torch.int16), want_out.view(torch.int16))
+    for leaf, w in zip(leaves, want):
+        a = leaf.grad.float()
+        b = w.float()
+        assert torch.linalg.norm(a - b) <= 2e-2 * torch.linalg.norm(b)
