@@ -159,7 +159,12 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   }
 
   // raw chunk data of this thread's staging tasks: a query task keeps one
-  // 16-byte chunk in d[0]; a key/value task keeps k(t), k(t+1), v(t), v(t+1)
+  // 16-byte chunk in d[0]; a key/value task keeps k(t), k(t+1), v(t), v(t+1).
+  // Tokens past the segment load the segment's last token (in bounds): the
+  // outputs of such query rows are not stored, and such key rows carry the
+  // weight 0 (stage), so their values never reach a stored output.  The
+  // loads sit in no branch that also writes their registers, so they stay
+  // in flight until stage consumes them.
   struct Raw {
     u32x4 d[CH][4];
   };
@@ -168,26 +173,23 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r.d[k][e] = u32x4{0u, 0u, 0u, 0u};
       if (task < NQT) {
-        const long long tok = t0 + (task >> 3);
-        if (tok < seg1) r.d[k][0] = *(const u32x4*)(Q + head + (size_t)tok * D + (task & 7) * 8);
+        const long long tok = min(t0 + (task >> 3), seg1 - 1);
+        r.d[k][0] = *(const u32x4*)(Q + head + (size_t)tok * D + (task & 7) * 8);
       } else if (task < NTASK) {
         const int kv = task - NQT;
         const int t = pair_token(kv >> 3), c8 = kv & 7;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const long long tok = t0 + t + h;
-          if (tok < seg1) {
-            r.d[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
-            r.d[k][2 + h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
-          }
+          const long long tok = min(t0 + t + h, seg1 - 1);
+          r.d[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
+          r.d[k][2 + h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
         }
       }
     }
   };
   auto stage = [&](const Raw& r, int buf, long long t0) {
+    wait_vm_loads();
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
@@ -464,10 +466,14 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   for (int i = 0; i < n_chunks; ++i) {
     const int buf = i & 1;
     const long long t0 = chunk_t0(i);
-    const bool more = i + 1 < n_chunks;
-    if (more) fetch(ra, chunk_t0(i + 1));
+    // the next chunk is fetched and staged on every pass (the last pass
+    // restages its own chunk into the idle buffer, which nothing reads):
+    // with no branch around the loads, every path waits for them inside
+    // stage, and the loop head does not wait on the previous chunk's stores
+    const long long tn = chunk_t0(min(i + 1, n_chunks - 1));
+    fetch(ra, tn);
     compute(buf);
-    if (more) stage(ra, buf ^ 1, chunk_t0(i + 1));
+    stage(ra, buf ^ 1, tn);
     __syncthreads();
     reduce_store(buf, t0);
     __syncthreads();

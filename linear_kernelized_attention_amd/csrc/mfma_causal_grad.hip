@@ -162,7 +162,12 @@ __global__ __launch_bounds__(NW * 64) void causal_grad_kernel(
   }
 
   // raw chunk data of this thread's staging tasks: an X task keeps its X and
-  // W chunks in d[0], d[1]; a Y task keeps y(t), y(t+1), z(t), z(t+1)
+  // W chunks in d[0], d[1]; a Y task keeps y(t), y(t+1), z(t), z(t+1).
+  // Tokens past the segment load the segment's last token (in bounds): X
+  // rows only reach their own outputs, which are not stored, and stage
+  // gives Y rows past the segment zero Z rows and zero zz, so they add
+  // nothing.  The loads sit in no branch that also writes their registers,
+  // so they stay in flight until stage consumes them.
   struct Raw {
     u32x4 d[CH][4];
     float s[CH][2];
@@ -172,32 +177,26 @@ __global__ __launch_bounds__(NW * 64) void causal_grad_kernel(
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r.d[k][e] = u32x4{0u, 0u, 0u, 0u};
-      r.s[k][0] = r.s[k][1] = 0.f;
       if (task < NXT) {
-        const long long tok = t0 + (task >> 3);
-        if (tok < seg1) {
-          r.d[k][0] = *(const u32x4*)(X + head + (size_t)tok * D + (task & 7) * 8);
-          r.d[k][1] = *(const u32x4*)(Wr + head + (size_t)tok * D + (task & 7) * 8);
-          if (!REV && (task & 7) == 0) r.s[k][0] = wzp[(size_t)bh * L + tok];
-        }
+        const long long tok = min(t0 + (task >> 3), seg1 - 1);
+        r.d[k][0] = *(const u32x4*)(X + head + (size_t)tok * D + (task & 7) * 8);
+        r.d[k][1] = *(const u32x4*)(Wr + head + (size_t)tok * D + (task & 7) * 8);
+        if (!REV) r.s[k][0] = wzp[(size_t)bh * L + tok];
       } else if (task < NTASK) {
         const int yt = task - NXT;
         const int t = pair_token(yt >> 3), c8 = yt & 7;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const long long tok = t0 + t + h;
-          if (tok < seg1) {
-            r.d[k][h] = *(const u32x4*)(Y + head + (size_t)tok * D + c8 * 8);
-            r.d[k][2 + h] = *(const u32x4*)(Zr + head + (size_t)tok * D + c8 * 8);
-            if (REV && c8 == 0) r.s[k][h] = zzp[(size_t)bh * L + tok];
-          }
+          const long long tok = min(t0 + t + h, seg1 - 1);
+          r.d[k][h] = *(const u32x4*)(Y + head + (size_t)tok * D + c8 * 8);
+          r.d[k][2 + h] = *(const u32x4*)(Zr + head + (size_t)tok * D + c8 * 8);
+          if (REV) r.s[k][h] = zzp[(size_t)bh * L + tok];
         }
       }
     }
   };
   auto stage = [&](const Raw& r, int buf, long long t0) {
+    wait_vm_loads();
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
@@ -235,8 +234,8 @@ __global__ __launch_bounds__(NW * 64) void causal_grad_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const bool valid = t0 + t + h < seg1;
-          zw[h] = (TRIG && !REV) ? (valid ? __builtin_amdgcn_exp2f(hs[h]) : 0.f) : 1.f;
-          zz[h] = REV ? r.s[k][h] : (valid ? zw[h] : 0.f);
+          zw[h] = valid ? ((TRIG && !REV) ? __builtin_amdgcn_exp2f(hs[h]) : 1.f) : 0.f;
+          zz[h] = valid ? (REV ? r.s[k][h] : zw[h]) : 0.f;
         }
         *(u32x4*)&Ys[buf][k_index(t, c8)] = r.d[k][0];
         *(u32x4*)&Ys[buf][k_index(t + 1, c8)] = r.d[k][1];
@@ -489,10 +488,13 @@ __global__ __launch_bounds__(NW * 64) void causal_grad_kernel(
   for (int i = 0; i < n_chunks; ++i) {
     const int buf = i & 1;
     const long long t0 = chunk_t0(i);
-    const bool more = i + 1 < n_chunks;
-    if (more) fetch(ra, chunk_t0(i + 1));
+    // the next chunk is fetched and staged on every pass (the last pass
+    // restages its own chunk into the idle buffer, which nothing reads), so
+    // no branch separates the loads from the wait in stage
+    const long long tn = chunk_t0(min(i + 1, n_chunks - 1));
+    fetch(ra, tn);
     compute(buf);
-    if (more) stage(ra, buf ^ 1, chunk_t0(i + 1));
+    stage(ra, buf ^ 1, tn);
     __syncthreads();
     reduce_store(buf, t0);
     __syncthreads();

@@ -62,6 +62,13 @@ __device__ inline bf16x8 pack8(const float* v) {
   return r;
 }
 
+// Wait until every vector-memory access of this wave has completed
+// (s_waitcnt with vmcnt 0, expcnt and lgkmcnt left open).  Staging code
+// that consumes a chunk's loads inside per-task branches calls it first:
+// the compiler then knows that no load is still in flight into those
+// registers, and the next chunk's loads need no wait of their own.
+__device__ inline void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8), each with its own L2.  Renumber blocks so that consecutive logical
 // blocks -- the blocks of one head, which read the same keys, values and
