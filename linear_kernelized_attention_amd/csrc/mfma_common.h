@@ -55,6 +55,26 @@ __device__ inline uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + the low or high bf16 half of the 32-bit word x, the sum rounded
+// once in float32: v_dot2c_f32_bf16 of x with the selector (1, 0) or (0, 1),
+// one instruction in place of a shift or mask and an add.  The selectors
+// are made by bf16_half_selectors and passed in registers: the packed word
+// 0x00003F80 must not become an inline constant, which the instruction
+// does not read as a bf16 pair.
+struct Bf16HalfSel {
+  uint32_t lo, hi;
+};
+__device__ inline Bf16HalfSel bf16_half_selectors() {
+  Bf16HalfSel s{0x00003F80u, 0x3F800000u};
+  asm("" : "+v"(s.lo), "+v"(s.hi));
+  return s;
+}
+__device__ inline float add_bf16_half(float acc, uint32_t x, uint32_t sel) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, sel),
+                                         acc, false);
+}
+
 __device__ inline bf16x8 pack8(const float* v) {
   bf16x8 r;
 #pragma unroll

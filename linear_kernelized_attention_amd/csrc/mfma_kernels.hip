@@ -164,62 +164,46 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
   // features fbase .. fbase + 15 at lane l, slots 4..7 the tile of features
   // fbase + 16 ..; for the fifth (z) fragment every lane of group g holds
   // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..].  fbase = 32 ks (relu) or
-  // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  All loads of a batch
-  // are issued before any is summed.
+  // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  Fragment blk = 5 ks + mt
+  // is 64 items (one per lane); wave w fills fragments w, w + NW, ..., so
+  // the fragment index is wave-uniform and its offsets are scalar work.
+  // All loads of a batch are issued before any is summed.
   {
     constexpr int NS = NKS * 5 * 64;
-    // element offsets of the two 4-element pieces of item (ks, mt, lane):
-    // value tiles of features fbase.. and fbase + 16.., or for the z tile
-    // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..]
-    auto item_off = [&](int item, int& second) {
-      const int ks = item / 320, mt = (item % 320) >> 6, l = item & 63;
+    constexpr int NBLK = NKS * 5;
+    const int wv = __builtin_amdgcn_readfirstlane(w);
+    // element offsets of the two 4-element pieces of fragment blk at this
+    // lane: value tiles of features fbase.. and fbase + 16.., or for the z
+    // tile z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..]
+    auto blk_off = [&](int blk, int& second) {
+      const int ks = blk / 5, mt = blk % 5;
       const int fbase = TRIG ? (ks & 1) * M + 32 * (ks >> 1) : 32 * ks;
       if (mt < 4) {
         second = 4 * TILE_ELEMS;
-        return vtile_off(fbase / 16, mt) + l * 4;
+        return vtile_off(fbase / 16, mt) + lane * 4;
       }
       second = 16;
-      return z_off(F, fbase + 4 * (l >> 4));
+      return z_off(F, fbase + 4 * g);
     };
     const uint16_t* pb = part + (size_t)bh * state_elems(F);
     if (nsum == 0) {
       // a prepared fragment image of this head's summed state
       const u32x4* src = (const u32x4*)(part + (size_t)bh * NS * 8);
       for (int i = tid; i < NS; i += NT) ((u32x4*)Sl)[i] = src[i];
-    } else if (nsum == 1) {
-      constexpr int BATCH = 10;
-      for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
-        u32x2 v[BATCH][2];
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-          int second;
-          const int off = item_off(min(i0 + b * NT, NS - 1), second);
-          v[b][0] = *(const u32x2*)(pb + off);
-          v[b][1] = *(const u32x2*)(pb + off + second);
-        }
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b)
-          if (i0 + b * NT < NS) {
-            u32x4 o;
-            o[0] = v[b][0][0];
-            o[1] = v[b][0][1];
-            o[2] = v[b][1][0];
-            o[3] = v[b][1][1];
-            *(u32x4*)(Sl + (size_t)(i0 + b * NT) * 8) = o;
-          }
-      }
     } else {
-      // nsum = 2..4, each a separately unrolled pass (no per-element
-      // selects): all loads of a batch, then the float32 sums in split order
+      // nsum = 1..4, each a separately unrolled pass (no per-element
+      // selects): all loads of a batch, then the float32 sums in split
+      // order, starting from split 0
       auto pass = [&](auto ns_tag) {
         constexpr int NSUM = decltype(ns_tag)::value;
-        constexpr int BATCH = 20 / NSUM;
-        for (int i0 = tid; i0 < NS; i0 += NT * BATCH) {
+        constexpr int BATCH = NSUM == 1 ? 10 : 20 / NSUM;
+        const Bf16HalfSel sel = bf16_half_selectors();
+        for (int b0 = wv; b0 < NBLK; b0 += NW * BATCH) {
           u32x2 v[BATCH][2][NSUM];
 #pragma unroll
           for (int b = 0; b < BATCH; ++b) {
             int second;
-            const int off = item_off(min(i0 + b * NT, NS - 1), second);
+            const int off = blk_off(min(b0 + b * NW, NBLK - 1), second);
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -228,22 +212,38 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
           }
 #pragma unroll
           for (int b = 0; b < BATCH; ++b) {
-            const int item = i0 + b * NT;
-            float sum[8];
+            const int blk = b0 + b * NW;
+            if (blk >= NBLK) break;
+            u32x4 o;
+            if (NSUM == 1) {
+              o[0] = v[b][0][0][0];
+              o[1] = v[b][0][0][1];
+              o[2] = v[b][1][0][0];
+              o[3] = v[b][1][0][1];
+            } else {
+              float sum[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+              for (int h = 0; h < 2; ++h)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                float acc = 0.f;
+                for (int u = 0; u < 2; ++u) {
+                  const uint32_t x0 = v[b][h][0][u];
+                  float lo = __uint_as_float(x0 << 16), hi = __uint_as_float(x0 & 0xffff0000u);
 #pragma unroll
-                for (int sp = 0; sp < NSUM; ++sp) acc += bf16_to_f32(((const uint16_t*)&v[b][h][sp])[r]);
-                sum[4 * h + r] = acc;
-              }
-            if (item < NS) *(bf16x8*)(Sl + (size_t)item * 8) = pack8(sum);
+                  for (int sp = 1; sp < NSUM; ++sp) {
+                    lo = add_bf16_half(lo, v[b][h][sp][u], sel.lo);
+                    hi = add_bf16_half(hi, v[b][h][sp][u], sel.hi);
+                  }
+                  sum[4 * h + 2 * u] = lo;
+                  sum[4 * h + 2 * u + 1] = hi;
+                }
+              o = __builtin_bit_cast(u32x4, pack8(sum));
+            }
+            *(u32x4*)(Sl + ((size_t)blk * 64 + lane) * 8) = o;
           }
         }
       };
-      if (nsum == 2) pass(std::integral_constant<int, 2>{});
+      if (nsum == 1) pass(std::integral_constant<int, 1>{});
+      else if (nsum == 2) pass(std::integral_constant<int, 2>{});
       else if (nsum == 3) pass(std::integral_constant<int, 3>{});
       else pass(std::integral_constant<int, 4>{});
     }
