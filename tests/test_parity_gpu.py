@@ -45,6 +45,10 @@ SMALL = [
     (1, 1, 150, 64, 160, "bf16"),
     # the fewest Omega rows on MFMA (one wave per block)
     (2, 1, 70, 64, 32, "bf16"),
+    # bidirectional MFMA readout summing 4 key-split partials (4 tiles of
+    # 128 keys, the last ragged); 1 x 3 x 257 sums 3, 1 x 2 x 200 (m = 96)
+    # sums 2, and 1 x 1 x 1000 goes through the split-sum kernel
+    (1, 2, 500, 64, 256, "bf16"),
 ]
 
 
