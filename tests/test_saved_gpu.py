@@ -109,23 +109,43 @@ def test_backward_saved(shape, kind, causal):
             assert e <= TOL[dtype], (path, name, e)
 
 
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_autograd_function(causal):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_function(dtype, causal, kind):
     # loss.backward() through the autograd wrapper gives the gradients of the
-    # direct backward call, and the forward gives favor_attention's output
-    shape = (2, 2, 200, 64, 64, "bf16")
-    B, H, L, d, m, dtype = shape
-    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=5)
-    gs, _ = I.output_grads(B, H, L, d, dtype, seed=5)
+    # direct backward call (within the bar), the forward gives
+    # favor_attention's output bit for bit, and the gradients stay within
+    # the bar of the oracle's
+    B, H, L, d, m = 2, 2, 200, 64, 64
+    for s in range(5, 25):
+        dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=s)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            if np.isfinite(O.favor_attention(q, k, v, W, kind, causal)).all():
+                break
+    else:
+        pytest.skip("no draw without 0/0 rows")
+    gs, g64 = I.output_grads(B, H, L, d, dtype, seed=s)
     g_dev = to_device(gs, dtype)
     leaves = [x.clone().requires_grad_(True) for x in dev[:3]]
-    out = F.favor_attention_fn(*leaves, dev[3], kind="trig", causal=causal)
+    out = F.favor_attention_fn(*leaves, dev[3], kind=kind, causal=causal)
     out.backward(g_dev)
-    want_out = F.favor_attention(*dev, kind="trig", causal=causal)
-    want = F.favor_attention_backward(*dev, g_dev, kind="trig", causal=causal)
+    want_out = F.favor_attention(*dev, kind=kind, causal=causal)
+    want = F.favor_attention_backward(*dev, g_dev, kind=kind, causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(out.detach().view(torch.int16), want_out.view(torch.int16))
-    for leaf, w in zip(leaves, want):
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t)
+    assert torch.equal(bits(out.detach()), bits(want_out))
+    ref = O.favor_attention_grad(q, k, v, W, g64, kind, causal, workers=O.default_workers())
+    for name, leaf, w, r in zip(("dq", "dk", "dv"), leaves, want, ref):
         a = leaf.grad.float()
         b = w.float()
-        assert torch.linalg.norm(a - b) <= 2e-2 * torch.linalg.norm(b)
+        assert torch.linalg.norm(a - b) <= TOL[dtype] * torch.linalg.norm(b), name
+        got = from_device(leaf.grad).reshape(-1, L, d)
+        rr = r.reshape(-1, L, d)
+        sc = ref[2].reshape(-1, L, d)   # dV's scale where a slice is ~0
+        e = 0.0
+        for i in range(got.shape[0]):
+            nr = np.linalg.norm(rr[i])
+            den = nr if nr > 1e-6 * np.linalg.norm(sc[i]) else np.linalg.norm(sc[i])
+            e = max(e, np.linalg.norm(got[i] - rr[i]) / den)
+        assert e <= TOL[dtype], (name, e)
