@@ -395,7 +395,7 @@ def main():
         for key, saved in (("head", False), ("c3_causal", False), ("c2_trig", False),
                            ("head", True), ("c3_causal", True)):
             wk = I.WORKLOADS[key]
-            sbw = bench_backward(F, I, wk, max(5, steps // 10), 2, saved)
+            sbw = bench_backward(F, I, wk, steps, max(3, args.warmup // 4), saved)
             fl = backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind)
             rp = F.favor_attention_backward_resolve_path(wk.B, wk.H, wk.L, wk.d, wk.m, wk.dtype,
                                                          wk.kind, wk.causal)
