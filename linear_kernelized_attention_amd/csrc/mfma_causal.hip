@@ -162,9 +162,12 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   // 16-byte chunk in d[0]; a key/value task keeps k(t), k(t+1), v(t), v(t+1).
   // Tokens past the segment load the segment's last token (in bounds): the
   // outputs of such query rows are not stored, and such key rows carry the
-  // weight 0 (stage), so their values never reach a stored output.  The
-  // loads sit in no branch that also writes their registers, so they stay
-  // in flight until stage consumes them.
+  // weight 0 (stage), so finite values never reach a stored output.  A
+  // non-finite last token reaches the earlier queries of its chunk through
+  // its own row anyway (masked scores multiply the value rows), and its
+  // copies reach nothing further.  The loads sit in no branch that also
+  // writes their registers, so they stay in flight until stage consumes
+  // them.
   struct Raw {
     u32x4 d[CH][4];
   };

@@ -151,6 +151,35 @@ def test_nonfinite_input_propagates():
         assert torch.isnan(out[0, 0, :, 3]).all()
 
 
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_causal_nonfinite_last_token_stays_local(which, kind):
+    # The causal output of token i depends on tokens j <= i only.  A NaN in
+    # the last token's key or value reaches that token's output.  The
+    # float32 path keeps every earlier output bit for bit; the MFMA path
+    # multiplies a chunk's value rows by masked scores, so the NaN may also
+    # reach the earlier tokens of its own 32-token chunk (NaN * 0), but no
+    # token of an earlier chunk.  L = 70 ends in a ragged chunk [64, 96).
+    B, H, L, d, m = 1, 2, 70, 64, 256
+    chunk0 = (L - 1) // 32 * 32
+    dev, _, _ = problem(B, H, L, d, m, "bf16", seed=L)
+    q, k, v, w = dev
+    bad = {"k": k, "v": v}[which].clone()
+    bad[:, :, L - 1, 5] = float("nan")
+    args = (bad, v) if which == "k" else (k, bad)
+    for path in _paths(B, H, L, d, m, "bf16", kind, True):
+        clean = F.favor_attention(q, k, v, w, kind=kind, causal=True, path=path)
+        out = F.favor_attention(q, *args, w, kind=kind, causal=True, path=path)
+        torch.cuda.synchronize()
+        keep = L - 1 if path == "generic" else chunk0
+        fin = torch.isfinite(clean.float()).all(dim=-1)[:, :, :keep]   # ReLU may have 0/0 rows
+        assert torch.equal(out[:, :, :keep][fin].view(torch.int16), clean[:, :, :keep][fin].view(torch.int16)), path
+        if not (kind == "relu" and which == "k"):
+            # (the device's ReLU features are max(P, 0) with IEEE maxNum: a
+            # NaN projection gives the feature 0, so a NaN key drops out)
+            assert torch.isnan(out[:, :, L - 1]).any(), path
+
+
 def test_profile_reports_kernels():
     dev, _, _ = problem(1, 2, 512, 64, 256, "bf16")
     for path in _paths(1, 2, 512, 64, 256, "bf16", "trig", False):
