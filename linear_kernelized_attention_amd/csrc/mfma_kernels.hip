@@ -114,10 +114,19 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
   constexpr int NOT = M / 16;
   constexpr int FT = TRIG ? 2 : 1;
   constexpr int NT = NW * 64;
+  // Beyond 8 Omega row pairs the state and the Omega~ fragments do not fit
+  // in LDS at once: the features are taken in FH passes of NPP row pairs
+  // (the k-steps and row tiles of a pass are contiguous), and the
+  // accumulators carry over from pass to pass.
+  constexpr int FH = NPAIR > 8 ? 2 : 1;
+  constexpr int NPP = NPAIR / FH;
+  constexpr int NKSP = NKS / FH;
+  constexpr int NOTP = NOT / FH;
+  static_assert(NPAIR % FH == 0 && NPP <= 8, "at most 8 Omega row pairs per pass");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  uint16_t* Sl = smem;                    // NKS * 5 fragments
-  uint16_t* Ol = smem + NKS * 5 * 512;    // NOT * 2 fragments
+  uint16_t* Sl = smem;                     // NKSP * 5 fragments
+  uint16_t* Ol = smem + NKSP * 5 * 512;    // NOTP * 2 fragments
 
   // query fragments first: their memory latency overlaps the rest
   const long long t0 = (long long)qblock * NW * QW + (long long)w * QW;
@@ -153,107 +162,6 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
       hq[nt] = 0.5f * LOG2E * ss * (1.0f / 8.0f);
     }
   }
-  // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
-  constexpr int NO = NOT * 2 * 64;
-  constexpr int CO = (NO + NT - 1) / NT;
-  u32x4 ov[CO];
-#pragma unroll
-  for (int k = 0; k < CO; ++k) ov[k] = ((const u32x4*)ofrag)[min(tid + k * NT, NO - 1)];
-
-  // S^T fragment (ks, mt), lane l = 16 g + c: slots 0..3 are the C tile of
-  // features fbase .. fbase + 15 at lane l, slots 4..7 the tile of features
-  // fbase + 16 ..; for the fifth (z) fragment every lane of group g holds
-  // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..].  fbase = 32 ks (relu) or
-  // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  Fragment blk = 5 ks + mt
-  // is 64 items (one per lane); wave w fills fragments w, w + NW, ..., so
-  // the fragment index is wave-uniform and its offsets are scalar work.
-  // All loads of a batch are issued before any is summed.
-  {
-    constexpr int NS = NKS * 5 * 64;
-    constexpr int NBLK = NKS * 5;
-    const int wv = __builtin_amdgcn_readfirstlane(w);
-    // element offsets of the two 4-element pieces of fragment blk at this
-    // lane: value tiles of features fbase.. and fbase + 16.., or for the z
-    // tile z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..]
-    auto blk_off = [&](int blk, int& second) {
-      const int ks = blk / 5, mt = blk % 5;
-      const int fbase = TRIG ? (ks & 1) * M + 32 * (ks >> 1) : 32 * ks;
-      if (mt < 4) {
-        second = 4 * TILE_ELEMS;
-        return vtile_off(fbase / 16, mt) + lane * 4;
-      }
-      second = 16;
-      return z_off(F, fbase + 4 * g);
-    };
-    const uint16_t* pb = part + (size_t)bh * state_elems(F);
-    if (nsum == 0) {
-      // a prepared fragment image of this head's summed state
-      const u32x4* src = (const u32x4*)(part + (size_t)bh * NS * 8);
-      for (int i = tid; i < NS; i += NT) ((u32x4*)Sl)[i] = src[i];
-    } else {
-      // nsum = 1..4, each a separately unrolled pass (no per-element
-      // selects): all loads of a batch, then the float32 sums in split
-      // order, starting from split 0
-      auto pass = [&](auto ns_tag) {
-        constexpr int NSUM = decltype(ns_tag)::value;
-        constexpr int BATCH = NSUM == 1 ? 10 : 20 / NSUM;
-        const Bf16HalfSel sel = bf16_half_selectors();
-        for (int b0 = wv; b0 < NBLK; b0 += NW * BATCH) {
-          u32x2 v[BATCH][2][NSUM];
-#pragma unroll
-          for (int b = 0; b < BATCH; ++b) {
-            int second;
-            const int off = blk_off(min(b0 + b * NW, NBLK - 1), second);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int sp = 0; sp < NSUM; ++sp)
-                v[b][h][sp] = *(const u32x2*)(pb + sp * split_stride + off + h * second);
-          }
-#pragma unroll
-          for (int b = 0; b < BATCH; ++b) {
-            const int blk = b0 + b * NW;
-            if (blk >= NBLK) break;
-            u32x4 o;
-            if (NSUM == 1) {
-              o[0] = v[b][0][0][0];
-              o[1] = v[b][0][0][1];
-              o[2] = v[b][1][0][0];
-              o[3] = v[b][1][0][1];
-            } else {
-              float sum[8];
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                  const uint32_t x0 = v[b][h][0][u];
-                  float lo = __uint_as_float(x0 << 16), hi = __uint_as_float(x0 & 0xffff0000u);
-#pragma unroll
-                  for (int sp = 1; sp < NSUM; ++sp) {
-                    lo = add_bf16_half(lo, v[b][h][sp][u], sel.lo);
-                    hi = add_bf16_half(hi, v[b][h][sp][u], sel.hi);
-                  }
-                  sum[4 * h + 2 * u] = lo;
-                  sum[4 * h + 2 * u + 1] = hi;
-                }
-              o = __builtin_bit_cast(u32x4, pack8(sum));
-            }
-            *(u32x4*)(Sl + ((size_t)blk * 64 + lane) * 8) = o;
-          }
-        }
-      };
-      if (nsum == 1) pass(std::integral_constant<int, 1>{});
-      else if (nsum == 2) pass(std::integral_constant<int, 2>{});
-      else if (nsum == 3) pass(std::integral_constant<int, 3>{});
-      else pass(std::integral_constant<int, 4>{});
-    }
-#pragma unroll
-    for (int k = 0; k < CO; ++k)
-      if (tid + k * NT < NO) *(u32x4*)(Ol + (size_t)(tid + k * NT) * 8) = ov[k];
-  }
-  __syncthreads();
-  // waves whose tokens all lie past L skip the work but stay for the
-  // barrier before the output staging
   const bool active = t0 < L;
 
   floatx4 acc[5][4];
@@ -321,21 +229,125 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(Sf[f][mt], Fr[f][nt], acc[mt][nt]);
   };
 
-  if (active) {
-    floatx4 P[2][4];
-    {
-      bf16x8 Of[2][2];
-      load_omega(0, Of);
-      proj(Of, P);
-    }
+#pragma unroll 1
+  for (int fh = 0; fh < FH; ++fh) {
+    // every wave has left the previous pass before its LDS is refilled
+    if (fh > 0) __syncthreads();
+    // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
+    constexpr int NO = NOTP * 2 * 64;   // per pass
+    constexpr int CO = (NO + NT - 1) / NT;
+    u32x4 ov[CO];
 #pragma unroll
-    for (int i = 0; i < NPAIR; ++i) {
-      bf16x8 Sf[FT][5], Of[2][2], Fr[FT][4];
-      load_s(i, Sf);
-      if (i + 1 < NPAIR) load_omega(i + 1, Of);
-      feat(P, Fr);
-      contract(Sf, Fr);
-      if (i + 1 < NPAIR) proj(Of, P);
+    for (int k = 0; k < CO; ++k) ov[k] = ((const u32x4*)ofrag)[fh * NO + min(tid + k * NT, NO - 1)];
+
+    // S^T fragment (ks, mt), lane l = 16 g + c: slots 0..3 are the C tile of
+    // features fbase .. fbase + 15 at lane l, slots 4..7 the tile of features
+    // fbase + 16 ..; for the fifth (z) fragment every lane of group g holds
+    // z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..].  fbase = 32 ks (relu) or
+    // s M + 32 i with i = ks / 2, s = ks % 2 (trig).  Fragment blk = 5 ks + mt
+    // is 64 items (one per lane); wave w fills fragments w, w + NW, ..., so
+    // the fragment index is wave-uniform and its offsets are scalar work.
+    // All loads of a batch are issued before any is summed.
+    {
+      constexpr int NS = NKSP * 5 * 64;   // per pass
+      constexpr int NBLK = NKSP * 5;
+      const int wv = __builtin_amdgcn_readfirstlane(w);
+      // element offsets of the two 4-element pieces of fragment blk at this
+      // lane: value tiles of features fbase.. and fbase + 16.., or for the z
+      // tile z[fbase + 4 g ..] and z[fbase + 16 + 4 g ..]
+      auto blk_off = [&](int blk, int& second) {
+        const int ks = blk / 5, mt = blk % 5;
+        const int fbase = TRIG ? (ks & 1) * M + 32 * (ks >> 1) : 32 * ks;
+        if (mt < 4) {
+          second = 4 * TILE_ELEMS;
+          return vtile_off(fbase / 16, mt) + lane * 4;
+        }
+        second = 16;
+        return z_off(F, fbase + 4 * g);
+      };
+      const uint16_t* pb = part + (size_t)bh * state_elems(F);
+      if (nsum == 0) {
+        // a prepared fragment image of this head's summed state
+        const u32x4* src = (const u32x4*)(part + ((size_t)bh * FH + fh) * NS * 8);
+        for (int i = tid; i < NS; i += NT) ((u32x4*)Sl)[i] = src[i];
+      } else {
+        // nsum = 1..4, each a separately unrolled pass (no per-element
+        // selects): all loads of a batch, then the float32 sums in split
+        // order, starting from split 0
+        auto pass = [&](auto ns_tag) {
+          constexpr int NSUM = decltype(ns_tag)::value;
+          constexpr int BATCH = NSUM == 1 ? 10 : 20 / NSUM;
+          const Bf16HalfSel sel = bf16_half_selectors();
+          for (int b0 = wv; b0 < NBLK; b0 += NW * BATCH) {
+            u32x2 v[BATCH][2][NSUM];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+              int second;
+              const int off = blk_off(fh * NBLK + min(b0 + b * NW, NBLK - 1), second);
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int sp = 0; sp < NSUM; ++sp)
+                  v[b][h][sp] = *(const u32x2*)(pb + sp * split_stride + off + h * second);
+            }
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+              const int blk = b0 + b * NW;
+              if (blk >= NBLK) break;
+              u32x4 o;
+              if (NSUM == 1) {
+                o[0] = v[b][0][0][0];
+                o[1] = v[b][0][0][1];
+                o[2] = v[b][1][0][0];
+                o[3] = v[b][1][0][1];
+              } else {
+                float sum[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                  for (int u = 0; u < 2; ++u) {
+                    const uint32_t x0 = v[b][h][0][u];
+                    float lo = __uint_as_float(x0 << 16), hi = __uint_as_float(x0 & 0xffff0000u);
+#pragma unroll
+                    for (int sp = 1; sp < NSUM; ++sp) {
+                      lo = add_bf16_half(lo, v[b][h][sp][u], sel.lo);
+                      hi = add_bf16_half(hi, v[b][h][sp][u], sel.hi);
+                    }
+                    sum[4 * h + 2 * u] = lo;
+                    sum[4 * h + 2 * u + 1] = hi;
+                  }
+                o = __builtin_bit_cast(u32x4, pack8(sum));
+              }
+              *(u32x4*)(Sl + ((size_t)blk * 64 + lane) * 8) = o;
+            }
+          }
+        };
+        if (nsum == 1) pass(std::integral_constant<int, 1>{});
+        else if (nsum == 2) pass(std::integral_constant<int, 2>{});
+        else if (nsum == 3) pass(std::integral_constant<int, 3>{});
+        else pass(std::integral_constant<int, 4>{});
+      }
+#pragma unroll
+      for (int k = 0; k < CO; ++k)
+        if (tid + k * NT < NO) *(u32x4*)(Ol + (size_t)(tid + k * NT) * 8) = ov[k];
+    }
+    __syncthreads();
+    if (active) {
+      floatx4 P[2][4];
+      {
+        bf16x8 Of[2][2];
+        load_omega(0, Of);
+        proj(Of, P);
+      }
+#pragma unroll
+      for (int i = 0; i < NPP; ++i) {
+        bf16x8 Sf[FT][5], Of[2][2], Fr[FT][4];
+        load_s(i, Sf);
+        if (i + 1 < NPP) load_omega(i + 1, Of);
+        feat(P, Fr);
+        contract(Sf, Fr);
+        if (i + 1 < NPP) proj(Of, P);
+      }
     }
   }
 
@@ -435,7 +447,10 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
 constexpr int RO_NW = 8;  // waves per readout block
 
 size_t readout_lds(const Problem& p) {
-  const size_t frags = ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t);
+  // per feature pass: more than 8 Omega row pairs take two passes
+  const int passes = p.m > 256 ? 2 : 1;
+  const size_t frags =
+      ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t) / passes;
   const size_t staging = (size_t)RO_NW * QW * OROW * sizeof(uint16_t);
   return frags > staging ? frags : staging;
 }
@@ -474,6 +489,13 @@ void launch_readout_m(const Problem& p, const Buffers& b, const uint16_t* part, 
     case 5: launch_readout<KIND, 5, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
     case 6: launch_readout<KIND, 6, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
     case 7: launch_readout<KIND, 7, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
+    case 16:
+      // m = 512 (two feature passes); the backward readouts never see it
+      if constexpr (MODE == RO_OUT) {
+        launch_readout<KIND, 16, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
+        break;
+      }
+      [[fallthrough]];
     default: launch_readout<KIND, 8, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat); break;
   }
 }
@@ -634,8 +656,11 @@ hipError_t run_causal_backward(const Problem& p, const Buffers& b, const BwdBuff
                                hipStream_t s, PhaseHook* hook);
 
 bool supports(const Problem& p) {
-  return p.dtype == DT_BF16 && p.d == D && p.m % 32 == 0 && p.m >= 32 && p.m <= 256 &&
-         lds_fits(p);
+  // m up to 256 on every path; m = 512 on the bidirectional forward (the
+  // readout takes its features in two passes; the causal kernels keep a
+  // wave per 32 Omega rows and stop at 8 waves)
+  const bool m_ok = (p.m % 32 == 0 && p.m >= 32 && p.m <= 256) || (p.m == 512 && !p.causal);
+  return p.dtype == DT_BF16 && p.d == D && m_ok && lds_fits(p);
 }
 
 size_t workspace_bytes(const Problem& p) {

@@ -49,6 +49,9 @@ SMALL = [
     # 128 keys, the last ragged); 1 x 3 x 257 sums 3, 1 x 2 x 200 (m = 96)
     # sums 2, and 1 x 1 x 1000 goes through the split-sum kernel
     (1, 2, 500, 64, 256, "bf16"),
+    # m = 512: the bidirectional MFMA readout in two feature passes (the
+    # causal and float32 cases run on the generic kernels)
+    (1, 2, 300, 64, 512, "bf16"),
 ]
 
 
@@ -105,6 +108,23 @@ def test_full_size_sampled_rows(name):
         got = _run(dev, w.kind, w.causal, path)[..., rows, :]
         err = slice_rel_err(got, ref)
         print(f"[{path}] {name} sampled rel={err:.3e}", flush=True)
+        assert err <= 2e-2
+
+
+@pytest.mark.parametrize("kind", ["trig", "positive"])
+def test_m512_long_sampled_rows(kind):
+    # the top of the pages' feature grid at a long sequence: B1 H4 L4096,
+    # m = 512, bidirectional (MFMA readout in two feature passes, four key
+    # splits summed in its prologue)
+    B, H, L, d, m = 1, 4, 4096, 64, 512
+    assert F.favor_attention_resolve_path(B, H, L, d, m, "bf16", kind, False) == "mfma"
+    dev, (q, k, v), W = problem(B, H, L, d, m, "bf16", seed=512)
+    rows = I.sample_rows(L, 256, seed=0)
+    ref = O.favor_rows(q, k, v, W, kind, False, rows)
+    for path in _paths(B, H, L, d, m, "bf16", kind, False):
+        got = _run(dev, kind, False, path)[..., rows, :]
+        err = slice_rel_err(got, ref)
+        print(f"[{path}] m512 {kind} sampled rel={err:.3e}", flush=True)
         assert err <= 2e-2
 
 
