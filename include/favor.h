@@ -74,7 +74,8 @@ typedef enum {
 
 /* Kernel family selection for favor_attention_ex (AUTO = the fastest path
  * that supports the request).  MFMA requires bf16, d = 64 and m a multiple
- * of 32 with m <= 256; GENERIC handles f32 and bf16 with d <= 64. */
+ * of 32 with m <= 256, or m = 512 for the bidirectional forward; GENERIC
+ * handles f32 and bf16 with d <= 64. */
 typedef enum { FAVOR_PATH_AUTO = 0, FAVOR_PATH_GENERIC = 1, FAVOR_PATH_MFMA = 2 } favor_path;
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
