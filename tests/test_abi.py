@@ -123,6 +123,24 @@ def test_resolve_path():
         F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False, "mfma")
 
 
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
+def test_resolve_path_feature_counts(kind):
+    # MFMA takes m a multiple of 32 up to 256 in both directions, and m = 512
+    # for the bidirectional forward only; everything else is generic
+    R, RB = F.favor_attention_resolve_path, F.favor_attention_backward_resolve_path
+    for m in (32, 96, 256):
+        for causal in (False, True):
+            assert R(1, 4, 4096, 64, m, "bf16", kind, causal) == "mfma"
+    assert R(1, 4, 4096, 64, 512, "bf16", kind, False) == "mfma"
+    assert R(1, 4, 4096, 64, 512, "bf16", kind, True) == "generic"
+    assert RB(1, 4, 4096, 64, 512, "bf16", kind, False) == "generic"
+    assert RB(1, 4, 4096, 64, 512, "bf16", kind, True) == "generic"
+    for m in (288, 384, 1024):
+        assert R(1, 4, 4096, 64, m, "bf16", kind, False) == "generic"
+    with pytest.raises(F.FavorError):
+        R(1, 4, 4096, 64, 512, "bf16", kind, True, "mfma")
+
+
 def test_linear_and_embed_argument_checks():
     lib = F.lib()
     assert lib.favor_linear_bf16(QA, KA, OA, 0, 64, 64, 0, 0, 0, None) == B.FAVOR_ERR_INVALID_ARG
