@@ -446,12 +446,12 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------- host
 constexpr int RO_NW = 8;  // waves per readout block
 
-size_t readout_lds(const Problem& p) {
+size_t readout_lds(const Problem& p, int nw = RO_NW) {
   // per feature pass: more than 8 Omega row pairs take two passes
   const int passes = p.m > 256 ? 2 : 1;
   const size_t frags =
       ((size_t)(p.F / 32) * 5 + (size_t)(p.m / 16) * 2) * 512 * sizeof(uint16_t) / passes;
-  const size_t staging = (size_t)RO_NW * QW * OROW * sizeof(uint16_t);
+  const size_t staging = (size_t)nw * QW * OROW * sizeof(uint16_t);
   return frags > staging ? frags : staging;
 }
 
@@ -465,16 +465,36 @@ void allow_full_lds(Kern kern) {
   (void)done;
 }
 
+template <int KIND, int NW, int NPAIR, int MODE>
+void launch_readout_nw(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
+                       int nsum, const uint16_t* ofrag, hipStream_t s, const uint16_t* G,
+                       float* bhat) {
+  auto kern = readout_kernel<KIND, NW, NPAIR, MODE>;
+  allow_full_lds(kern);
+  const long long nb = (p.L + NW * QW - 1) / (NW * QW);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(NW * 64), readout_lds(p, NW), s,
+                     (const uint16_t*)b.q, ofrag, part, split_stride, nsum, (uint16_t*)b.out, p.L,
+                     p.BH, G, bhat);
+}
+
+// RO_NW waves (64 queries each) per block.  One block fills a CU (its LDS),
+// so when such blocks would leave CUs idle and the sequence is long enough
+// for half-size blocks to double their number, the forward takes blocks of
+// RO_NW / 2 waves instead.
 template <int KIND, int NPAIR, int MODE>
 void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
                     int nsum, const uint16_t* ofrag, hipStream_t s, const uint16_t* G,
                     float* bhat) {
-  auto kern = readout_kernel<KIND, RO_NW, NPAIR, MODE>;
-  allow_full_lds(kern);
-  const long long nb = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(RO_NW * 64), readout_lds(p), s,
-                     (const uint16_t*)b.q, ofrag, part, split_stride, nsum, (uint16_t*)b.out, p.L,
-                     p.BH, G, bhat);
+  if constexpr (MODE == RO_OUT) {
+    constexpr int HW = RO_NW / 2;
+    const long long nb_full = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
+    const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
+    if (nb_full * p.BH < 256 && nb_half > nb_full) {
+      launch_readout_nw<KIND, HW, NPAIR, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
+      return;
+    }
+  }
+  launch_readout_nw<KIND, RO_NW, NPAIR, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
 }
 
 template <int KIND, int MODE = RO_OUT>
