@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void dphi_prep_kernel(const uint16_t* __restri
     }
 }
 
-template <int KIND, int NPAIR>
-__global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
+template <int KIND, int NPAIR, int NW = DPHI_NW>
+__global__ __launch_bounds__(NW * 64) void dphi_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ ofrag, DphiPrep prep,
     const uint16_t* __restrict__ Wv, const float* __restrict__ wz,
     uint16_t* __restrict__ DX, int L, long long BH, int keys) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
   constexpr int F = TRIG ? 2 * M : M;
   constexpr int NFT = F / 16;     // 16-feature tiles
   constexpr int NOT = M / 16;     // Omega row tiles
-  constexpr int NT = DPHI_NW * 64;
+  constexpr int NT = NW * 64;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   constexpr bool RELU = KIND == KIND_RELU;
   uint16_t* Mr = smem;                              // [NFT][2][64][8]
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
   const int blk = (int)(lb % nx);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const long long t0 = (long long)blk * DPHI_NW * QW + (long long)w * QW;
+  const long long t0 = (long long)blk * NW * QW + (long long)w * QW;
   const size_t head = (size_t)bh * L * D;
 
   // M row fragments and z (prepared per head), the Omega~ fragments, the
@@ -330,23 +330,37 @@ __global__ __launch_bounds__(DPHI_NW * 64) void dphi_kernel(
   }
 }
 
-template <int KIND, int NPAIR>
-hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
-                         const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
-                         bool keys, hipStream_t s) {
+template <int KIND, int NPAIR, int NW>
+hipError_t launch_dphi_nw(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
+                          const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                          bool keys, hipStream_t s) {
   constexpr int M = 32 * NPAIR;
   constexpr int F = KIND == KIND_TRIG ? 2 * M : M;
-  auto kern = dphi_kernel<KIND, NPAIR>;
+  auto kern = dphi_kernel<KIND, NPAIR, NW>;
   static const bool attr = [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return true;
   }();
   (void)attr;
-  const long long nb = (p.L + DPHI_NW * QW - 1) / (DPHI_NW * QW);
+  const long long nb = (p.L + NW * QW - 1) / (NW * QW);
   const size_t lds = dphi_lds_bytes<M, F, KIND == KIND_RELU>();
-  hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(DPHI_NW * 64), lds, s,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(NW * 64), lds, s,
                      X, ofrag, prep, Wv, wz, DX, p.L, p.BH, keys ? 1 : 0);
   return hipGetLastError();
+}
+
+// DPHI_NW waves per block, or half as many when full blocks would leave CUs
+// idle (one block fills a CU's LDS) and halving doubles their number.
+template <int KIND, int NPAIR>
+hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
+                         const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
+                         bool keys, hipStream_t s) {
+  constexpr int HW = DPHI_NW / 2;
+  const long long nb_full = (p.L + DPHI_NW * QW - 1) / (DPHI_NW * QW);
+  const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
+  if (nb_full * p.BH < 256 && nb_half > nb_full)
+    return launch_dphi_nw<KIND, NPAIR, HW>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+  return launch_dphi_nw<KIND, NPAIR, DPHI_NW>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
 }
 
 template <int KIND>

@@ -479,20 +479,18 @@ void launch_readout_nw(const Problem& p, const Buffers& b, const uint16_t* part,
 
 // RO_NW waves (64 queries each) per block.  One block fills a CU (its LDS),
 // so when such blocks would leave CUs idle and the sequence is long enough
-// for half-size blocks to double their number, the forward takes blocks of
-// RO_NW / 2 waves instead.
+// for half-size blocks to double their number, blocks of RO_NW / 2 waves
+// are taken instead.
 template <int KIND, int NPAIR, int MODE>
 void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, long long split_stride,
                     int nsum, const uint16_t* ofrag, hipStream_t s, const uint16_t* G,
                     float* bhat) {
-  if constexpr (MODE == RO_OUT) {
-    constexpr int HW = RO_NW / 2;
-    const long long nb_full = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
-    const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
-    if (nb_full * p.BH < 256 && nb_half > nb_full) {
-      launch_readout_nw<KIND, HW, NPAIR, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
-      return;
-    }
+  constexpr int HW = RO_NW / 2;
+  const long long nb_full = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
+  const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
+  if (nb_full * p.BH < 256 && nb_half > nb_full) {
+    launch_readout_nw<KIND, HW, NPAIR, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
+    return;
   }
   launch_readout_nw<KIND, RO_NW, NPAIR, MODE>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
 }
