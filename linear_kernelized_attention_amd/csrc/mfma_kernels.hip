@@ -231,7 +231,9 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
 
 #pragma unroll 1
   for (int fh = 0; fh < FH; ++fh) {
-    // every wave has left the previous pass before its LDS is refilled
+    // every wave has left the previous pass before its LDS is refilled; the
+    // pass holds global fragments fh * NBLK + b at LDS slot b, and its loop
+    // counts its own row pairs (global pair fh * NPP + i)
     if (fh > 0) __syncthreads();
     // Omega~ fragment i: lane i % 64, column half (i / 64) % 2, rows 16 (i / 128) ..
     constexpr int NO = NOTP * 2 * 64;   // per pass
