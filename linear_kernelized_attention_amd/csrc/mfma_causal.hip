@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   constexpr int KS = TRIG ? 2 : 1;    // 32-feature k-steps per wave
   constexpr int NT = NW * 64;
   constexpr int NQT = CT * 8;         // query staging tasks (token, 8 columns)
-  constexpr int NKV = CT / 2 * 8;     // key/value staging tasks (token pair, 8 columns)
+  constexpr int NKV = CT / 2 * 16;    // key/value staging tasks (token pair, 4 columns)
   constexpr int NTASK = NQT + NKV;
   constexpr int CH = (NTASK + NT - 1) / NT;
 
@@ -159,17 +159,20 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   }
 
   // raw chunk data of this thread's staging tasks: a query task keeps one
-  // 16-byte chunk in d[0]; a key/value task keeps k(t), k(t+1), v(t), v(t+1).
-  // Tokens past the segment load the segment's last token (in bounds): the
-  // outputs of such query rows are not stored, and such key rows carry the
-  // weight 0 (stage), so finite values never reach a stored output.  A
-  // non-finite last token reaches the earlier queries of its chunk through
-  // its own row anyway (masked scores multiply the value rows), and its
-  // copies reach nothing further.  The loads sit in no branch that also
-  // writes their registers, so they stay in flight until stage consumes
-  // them.
+  // 16-byte chunk (token, 8 columns); a key/value task keeps 8-byte chunks
+  // (4 columns) of k(t), k(t+1), v(t), v(t+1) -- with 4 columns per task the
+  // key/value staging spreads over as many waves as the query staging, one
+  // of each per SIMD.  Tokens past the segment load the segment's last token
+  // (in bounds): the outputs of such query rows are not stored, and such
+  // key rows carry the weight 0 (stage), so finite values never reach a
+  // stored output.  A non-finite last token reaches the earlier queries of
+  // its chunk through its own row anyway (masked scores multiply the value
+  // rows), and its copies reach nothing further.  The two task kinds load
+  // into separate registers and the loads sit in no branch that also writes
+  // them, so they stay in flight until stage consumes them.
   struct Raw {
-    u32x4 d[CH][4];
+    u32x4 q[CH];
+    u32x2 kv[CH][4];
   };
   Raw ra;
   auto fetch = [&](Raw& r, long long t0) {
@@ -178,15 +181,15 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       const int task = tid + k * NT;
       if (task < NQT) {
         const long long tok = min(t0 + (task >> 3), seg1 - 1);
-        r.d[k][0] = *(const u32x4*)(Q + head + (size_t)tok * D + (task & 7) * 8);
+        r.q[k] = *(const u32x4*)(Q + head + (size_t)tok * D + (task & 7) * 8);
       } else if (task < NTASK) {
         const int kv = task - NQT;
-        const int t = pair_token(kv >> 3), c8 = kv & 7;
+        const int t = pair_token(kv >> 4), c4 = kv & 15;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const long long tok = min(t0 + t + h, seg1 - 1);
-          r.d[k][h] = *(const u32x4*)(K + head + (size_t)tok * D + c8 * 8);
-          r.d[k][2 + h] = *(const u32x4*)(V + head + (size_t)tok * D + c8 * 8);
+          r.kv[k][h] = *(const u32x2*)(K + head + (size_t)tok * D + c4 * 4);
+          r.kv[k][2 + h] = *(const u32x2*)(V + head + (size_t)tok * D + c4 * 4);
         }
       }
     }
@@ -196,46 +199,59 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int task = tid + k * NT;
-      const bool kvtask = task >= NQT && task < NTASK;
-      float ct[2], hs[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // squared norms: of the keys, and (positive map) of the query chunk
-        const bool use = kvtask || (QOFF && h == 0 && task < NQT);
-        const uint16_t* kv = (const uint16_t*)&r.d[k][h];
+      const bool qtask = task < NQT, kvtask = !qtask && task < NTASK;
+      // squared norms, summed over the lanes that hold a row (every lane
+      // takes part): the query chunk's (positive map, and the trig weight
+      // of the reversed walk) over 8 lanes, the keys' over 16
+      float hq = 0.f;
+      if (QOFF) {
+        const uint16_t* x8 = (const uint16_t*)&r.q[k];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float x = use ? bf16_to_f32(kv[i]) : 0.f;
+          const float x = qtask ? bf16_to_f32(x8[i]) : 0.f;
           ss = fmaf(x, x, ss);
         }
-        ss = octet_sum(ss);
-        ct[h] = TRIG && !REV ? __expf(0.5f * ss * knorm_scale) : 1.f;
-        hs[h] = 0.5f * LOG2E * ss * knorm_scale;
+        hq = 0.5f * LOG2E * octet_sum(ss) * knorm_scale;
       }
-      if (task < NQT) {
-        *(u32x4*)&Qs[buf][k_index(task >> 3, task & 7)] = r.d[k][0];
-        if (QOFF && (task & 7) == 0) Hq[buf][task >> 3] = hs[0];
-      } else if (task < NTASK) {
+      float ct[2], hk[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t* x4 = (const uint16_t*)&r.kv[k][h];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = kvtask ? bf16_to_f32(x4[i]) : 0.f;
+          ss = fmaf(x, x, ss);
+        }
+        ss = sixteen_sum(ss);
+        ct[h] = TRIG && !REV ? __expf(0.5f * ss * knorm_scale) : 1.f;
+        hk[h] = 0.5f * LOG2E * ss * knorm_scale;
+      }
+      if (qtask) {
+        *(u32x4*)&Qs[buf][k_index(task >> 3, task & 7)] = r.q[k];
+        if (QOFF && (task & 7) == 0) Hq[buf][task >> 3] = hq;
+      } else if (kvtask) {
         const int kv = task - NQT;
-        const int q = kv >> 3, c8 = kv & 7;
+        const int q = kv >> 4, c4 = kv & 15;
         const int t = pair_token(q);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           if (t0 + t + h >= seg1) ct[h] = 0.f;
-        *(u32x4*)&Ks[buf][k_index(t, c8)] = r.d[k][0];
-        *(u32x4*)&Ks[buf][k_index(t + 1, c8)] = r.d[k][1];
-        if (POS && c8 == 0) {
-          Hk[buf][t] = hs[0];
-          Hk[buf][t + 1] = hs[1];
+        // 4 columns: half c4 % 2 of the (swizzled) 8-column chunk c4 / 2
+        *(u32x2*)&Ks[buf][k_index(t, c4 >> 1) + 4 * (c4 & 1)] = r.kv[k][0];
+        *(u32x2*)&Ks[buf][k_index(t + 1, c4 >> 1) + 4 * (c4 & 1)] = r.kv[k][1];
+        if (POS && c4 == 0) {
+          Hk[buf][t] = hk[0];
+          Hk[buf][t + 1] = hk[1];
         }
-        const uint16_t* v0 = (const uint16_t*)&r.d[k][2];
-        const uint16_t* v1 = (const uint16_t*)&r.d[k][3];
+        const uint16_t* v0 = (const uint16_t*)&r.kv[k][2];
+        const uint16_t* v1 = (const uint16_t*)&r.kv[k][3];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *(uint32_t*)&Vt[buf][ct_index(c8 * 8 + i, 2 * q)] =
+        for (int i = 0; i < 4; ++i)
+          *(uint32_t*)&Vt[buf][ct_index(c4 * 4 + i, 2 * q)] =
               pack2(bf16_to_f32(v0[i]) * ct[0], bf16_to_f32(v1[i]) * ct[1]);
-        if (c8 == 0) *(uint32_t*)&Vt[buf][ct_index(D, 2 * q)] = pack2(ct[0], ct[1]);
+        if (c4 == 0) *(uint32_t*)&Vt[buf][ct_index(D, 2 * q)] = pack2(ct[0], ct[1]);
       }
     }
   };

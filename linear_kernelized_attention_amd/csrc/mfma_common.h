@@ -156,6 +156,13 @@ __device__ inline float octet_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
   return x;
 }
+// Sum over each aligned group of 16 lanes (a DPP row): the 8-lane sums,
+// then each lane adds the mirrored lane 15 - i of its row, which lies in
+// the other group of 8.
+__device__ inline float sixteen_sum(float x) {
+  x = octet_sum(x);
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+}
 
 // One key task = (head bh, token split, feature part), run by one block of
 // NW waves; wave w owns the 16 Omega rows r0 = part * 16 NW + 16 w .. +15.
