@@ -73,6 +73,25 @@ def test_forward_den(shape, kind, causal):
 
 
 @pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
+def test_forward_den_m512(kind):
+    # m = 512: the bidirectional MFMA readout takes its features in two
+    # passes; its row normalisers against the oracle's feature maps
+    B, H, L, d, m, dtype = 1, 2, 300, 64, 512, "bf16"
+    assert F.favor_attention_resolve_path(B, H, L, d, m, dtype, kind, False) == "mfma"
+    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=7)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        if not np.isfinite(O.favor_attention(q, k, v, W, kind, False)).all():
+            pytest.skip("0/0 row in the forward (ReLU)")
+    ref = _oracle_den(q, k, W, kind, False)
+    for path in ("generic", "mfma"):
+        out, den = F.favor_attention(*dev, kind=kind, causal=False, path=path, den=True)
+        torch.cuda.synchronize()
+        err = _rel(den.cpu().numpy().astype(np.float64), ref)
+        print(f"[{path}] m512 {kind} den rel = {err:.2e}", flush=True)
+        assert err <= TOL[dtype], (path, err)
+
+
+@pytest.mark.parametrize("kind", ["trig", "relu", "positive"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES[2:] + [(4, 8, 1024, 64, 256, "bf16")],
                          ids=IDS[2:] + ["4x8x1024_d64_m256_bf16"])
