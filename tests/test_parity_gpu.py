@@ -112,11 +112,12 @@ def test_full_size_sampled_rows(name):
 
 
 @pytest.mark.parametrize("kind", ["trig", "positive"])
-def test_m512_long_sampled_rows(kind):
-    # the top of the pages' feature grid at a long sequence: B1 H4 L4096,
-    # m = 512, bidirectional (MFMA readout in two feature passes, four key
-    # splits summed in its prologue)
-    B, H, L, d, m = 1, 4, 4096, 64, 512
+@pytest.mark.parametrize("BH", [(1, 4), (4, 8)], ids=["B1H4", "B4H8"])
+def test_m512_long_sampled_rows(BH, kind):
+    # the top of the pages' feature grid at a long sequence: L4096, m = 512,
+    # bidirectional (MFMA readout in two feature passes).  B1 H4 runs
+    # 4-wave readout blocks, B4 H8 the 8-wave ones.
+    (B, H), L, d, m = BH, 4096, 64, 512
     assert F.favor_attention_resolve_path(B, H, L, d, m, "bf16", kind, False) == "mfma"
     dev, (q, k, v), W = problem(B, H, L, d, m, "bf16", seed=512)
     rows = I.sample_rows(L, 256, seed=0)
