@@ -211,3 +211,38 @@ def test_block_same_token_same_row():
     for t in np.unique(ids):
         rows = y[0, ids == t]
         assert np.allclose(rows, rows[:1], rtol=1e-12, atol=1e-15)
+
+
+def test_block_head_split_and_orientation():
+    # Two heads of width 64 in a 128-wide block.  J maps embedding dims
+    # 64..127 onto output columns 0..63 (J[64 + i, i] = 1), so with the
+    # x W convention Q = K = X J holds X[:, 64:] in head 0's columns
+    # [0, 64) and zeros in head 1's columns [64, 128).  With the trig map
+    # phi(0) is the same vector for every token, so head 1 attends
+    # uniformly: each of its rows is the mean of its value rows.  W_o = J
+    # then puts head 1's output in Y[:, :64] and zeros in Y[:, 64:].  A
+    # column-interleaved head split (head h = columns h::2), X W^T in place
+    # of X W, or concat(heads) W_o^T each break one of these equalities.
+    rng = np.random.default_rng(5)
+    E, H, L = 128, 2, 48
+    ids = rng.integers(0, 26, size=(2, L))
+    emb = rng.standard_normal((26, E)) * 0.4
+    J = np.zeros((E, E))
+    J[64 + np.arange(64), np.arange(64)] = 1.0
+    wv = rng.standard_normal((E, E)) * 0.3
+    dr = I.omega_draws(64, 64, seed=2)
+    W = O.orthogonal_random_features(dr.gaussian, dr.radii, 64)
+    y = O.performer_block(ids, emb, J, J, wv, J, W, heads=H, kind="trig")
+    X = emb[ids]
+    head1_mean = X.mean(axis=1) @ wv[:, 64:]          # [B, 64]
+    assert _rel(y[:, :, :64], np.broadcast_to(head1_mean[:, None, :], (2, L, 64))) <= 1e-12
+    assert np.all(y[:, :, 64:] == 0.0)
+    # W_o = J^T instead routes head 0 to Y[:, 64:]: FAVOR of the tokens'
+    # upper embedding halves attending to each other, with values X wv[:, :64]
+    y0 = O.performer_block(ids, emb, J, J, wv, J.T, W, heads=H, kind="trig")
+    Xu = X[:, :, 64:][:, None]
+    ref0 = O.favor_attention(Xu, Xu, (X @ wv[:, :64])[:, None], W, "trig")[:, 0]
+    assert _rel(y0[:, :, 64:], ref0) <= 1e-12
+    assert np.all(y0[:, :, :64] == 0.0)
+    # and head 0 is not uniform (the check above has teeth)
+    assert np.ptp(ref0, axis=1).max() > 1e-3

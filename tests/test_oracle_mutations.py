@@ -85,8 +85,28 @@ def orthogonal_ok():
     return np.abs(blk @ blk.T - np.eye(8)).max() <= 1e-12
 
 
+def block_wiring_ok():
+    # the masked-LM block's head split and weight orientation (the same
+    # construction as tests/test_oracle_identities.py::
+    # test_block_head_split_and_orientation): Q = K = X J sends head 1
+    # zero queries and keys, so head 1 attends uniformly, and W_o = J
+    # routes head 1 to Y[:, :64]
+    r = np.random.default_rng(6)
+    E, L = 128, 24
+    ids = r.integers(0, 26, size=(1, L))
+    emb = r.standard_normal((26, E)) * 0.4
+    J = np.zeros((E, E))
+    J[64 + np.arange(64), np.arange(64)] = 1.0
+    wv = r.standard_normal((E, E)) * 0.3
+    W = _omega(64, 64, 4)
+    y = O.performer_block(ids, emb, J, J, wv, J, W, heads=2, kind="trig")
+    mean1 = emb[ids].mean(axis=1) @ wv[:, 64:]
+    return bool(np.allclose(y[:, :, :64], mean1[:, None, :], rtol=1e-10, atol=1e-14)
+                and np.all(y[:, :, 64:] == 0.0))
+
+
 ALL_PINS = [unbiased_trig_ok, unbiased_positive_ok, arccos_relu_ok, zero_features_ok,
-            causal_masked_ok, constant_values_ok, orthogonal_ok]
+            causal_masked_ok, constant_values_ok, orthogonal_ok, block_wiring_ok]
 
 
 def test_real_oracle_passes_every_pin():
@@ -170,6 +190,29 @@ def _bidir_no_normaliser(q, k, v, Omega, kind):
     return phq @ (phk.T @ v)
 
 
+def _block_variant(split_interleaved=False, w_transposed=False, wo_transposed=False):
+    def block(ids, embed, wq, wk, wv, wo, Omega, heads, kind="relu", workers=None):
+        X = np.asarray(embed, float)[np.asarray(ids)]
+        B, L, E = X.shape
+        dh = E // heads
+        tr = (lambda w: np.asarray(w, float).T) if w_transposed else (lambda w: np.asarray(w, float))
+
+        def split(Y):
+            if split_interleaved:   # head h = columns h, h + heads, ...
+                return Y.reshape(B, L, dh, heads).transpose(0, 3, 1, 2)
+            return Y.reshape(B, L, heads, dh).transpose(0, 2, 1, 3)
+
+        Q, K, V = split(X @ tr(wq)), split(X @ tr(wk)), split(X @ tr(wv))
+        Oh = O.favor_attention(Q, K, V, Omega, kind)
+        if split_interleaved:
+            Oc = Oh.transpose(0, 2, 3, 1).reshape(B, L, E)
+        else:
+            Oc = Oh.transpose(0, 2, 1, 3).reshape(B, L, E)
+        wo = np.asarray(wo, float)
+        return Oc @ (wo.T if wo_transposed else wo)
+    return block
+
+
 MUTANTS = {
     "trig without exp(|x|^2/2)": ("feature_map", _fm_no_norm_factor),
     "d^-1/2 instead of d^-1/4": ("feature_map", _fm_wrong_scale),
@@ -181,6 +224,9 @@ MUTANTS = {
     "ORF without Gram-Schmidt": ("orthogonal_random_features", _orf_no_orthogonalisation),
     "exclusive causal prefix": ("_causal_head", _causal_exclusive),
     "no D^-1 normaliser": ("_bidirectional_head", _bidir_no_normaliser),
+    "block heads interleaved": ("performer_block", _block_variant(split_interleaved=True)),
+    "block X W^T": ("performer_block", _block_variant(w_transposed=True)),
+    "block concat W_o^T": ("performer_block", _block_variant(wo_transposed=True)),
 }
 
 
