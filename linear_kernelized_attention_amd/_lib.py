@@ -14,7 +14,9 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfavor.so")
+# FAVOR_LIB may name another build of the same library (the host-sanitizer
+# build that the ABI tests load in a child process)
+LIB_PATH = os.environ.get("FAVOR_LIB") or os.path.join(PKG, "libfavor.so")
 
 FAVOR_OK = 0
 FAVOR_ERR_INVALID_ARG = -1
