@@ -15,8 +15,10 @@
  * Conventions shared by every entry point
  *  - All tensor pointers are device memory owned by the caller, except
  *    where an argument is documented as host memory.  The library never
- *    allocates or frees device memory and keeps no mutable global state;
- *    concurrent calls on different streams are safe.
+ *    allocates or frees device memory.  Apart from favor_attention_noalloc
+ *    (a fixed scratch array per device, shared by its calls) it keeps no
+ *    mutable global state, and concurrent calls on different streams are
+ *    safe.
  *  - Tensors are dense row-major.  Attention tensors are [B, H, L, d] with
  *    d fastest; Omega is [m, d] float32 and shared by every (b, h).
  *  - Device pointers (tensors and workspace) must be 16-byte aligned (the
@@ -135,6 +137,32 @@ int favor_attention(const void* Q, const void* K, const void* V, const float* Om
 int favor_attention_ex(const void* Q, const void* K, const void* V, const float* Omega, void* out,
                        int B, int H, int L, int d, int m, int dtype, int kind, int causal,
                        void* workspace, size_t workspace_bytes, void* stream, int path);
+
+/*
+ * favor_attention_noalloc -- favor_attention_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace argument;
+ * the kernels' scratch (the same buffers favor_attention_ex takes as its
+ * workspace) is one fixed array of FAVOR_NOALLOC_SCRATCH_BYTES inside the
+ * library, of which each device the library runs on holds its own copy
+ * until the process ends.  The call allocates and frees nothing; the
+ * first call on a device looks up that device's copy once.
+ *   Arguments, layouts, results and errors as favor_attention_ex (the
+ *   caller still owns Q, K, V, Omega and out).  The device is the one
+ *   `stream` belongs to (the current device for a NULL stream).
+ *   A request whose workspace (favor_attention_workspace_bytes_ex) exceeds
+ *   FAVOR_NOALLOC_SCRATCH_BYTES returns FAVOR_ERR_WORKSPACE before
+ *   anything is enqueued.
+ *   Every call on one device shares that device's scratch, and its
+ *   contents are whatever the last call left (the kernels never read
+ *   scratch they have not written in the same call): calls that overlap
+ *   in time on one device -- on different streams, or from different host
+ *   threads -- race and must be ordered by the caller.
+ */
+#define FAVOR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int favor_attention_noalloc(const void* Q, const void* K, const void* V, const float* Omega,
+                            void* out, int B, int H, int L, int d, int m, int dtype, int kind,
+                            int causal, void* stream, int path);
 
 /*
  * favor_attention_train: favor_attention_ex that also writes the row

@@ -4,7 +4,8 @@ The Python layer is a thin ctypes binding over libfavor.so; torch supplies
 device memory and streams only.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, FavorError, LIB_PATH, favor_attention, favor_attention_resolve_path,
+    EXPORTS, FavorError, LIB_PATH, favor_attention, favor_attention_noalloc,
+    favor_attention_resolve_path,
     favor_attention_backward, favor_attention_backward_resolve_path,
     favor_attention_backward_workspace_bytes,
     favor_attention_workspace_bytes, favor_embed_bf16, favor_linear_bf16, favor_orf_omega,

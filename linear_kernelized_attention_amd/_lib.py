@@ -39,6 +39,7 @@ EXPORTS = (
     "favor_attention_train", "favor_attention_backward_saved",
     "favor_attention_backward_workspace_bytes", "favor_attention_backward",
     "favor_attention_backward_workspace_bytes_ex", "favor_attention_backward_ex",
+    "favor_attention_noalloc",
 )
 
 
@@ -75,6 +76,7 @@ def _declare(lib: ctypes.CDLL) -> None:
         "favor_attention_backward_ex": (i, [p] * 8 + [i] * 8 + [p, z, p, i]),
         "favor_attention_train": (i, [p] * 6 + [i] * 8 + [p, z, p, i]),
         "favor_attention_backward_saved": (i, [p] * 10 + [i] * 8 + [p, z, p, i]),
+        "favor_attention_noalloc": (i, [p, p, p, p, p] + [i] * 8 + [p, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +220,26 @@ def favor_attention(q, k, v, omega, kind: str = "trig", causal: bool = False, pa
         raise ValueError("den must be a contiguous float32 [B, H, L] tensor")
     _check(lib().favor_attention_train(*args[:5], den.data_ptr(), *args[5:]), "favor_attention_train")
     return out, den
+
+
+def favor_attention_noalloc(q, k, v, omega, kind: str = "trig", causal: bool = False,
+                            path: str = "auto", out=None):
+    """favor_attention through the entry point that allocates nothing: the
+    library's fixed per-device scratch replaces the workspace (calls that
+    overlap in time on one device race; see include/favor.h)."""
+    import torch
+    _validate(q, k, v, omega)
+    B, H, L, d = q.shape
+    m = omega.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    _check(lib().favor_attention_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
+                                         out.data_ptr(), B, H, L, d, m, _torch_dtype_code(q),
+                                         KIND[kind], int(bool(causal)), _stream_ptr(q.device),
+                                         PATH[path]), "favor_attention_noalloc")
+    return out
 
 
 def favor_attention_backward_workspace_bytes(B, H, L, d, m, dtype="bf16", kind="trig",

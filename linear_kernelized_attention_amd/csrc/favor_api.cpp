@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <vector>
 
 #include "favor_internal.h"
@@ -185,9 +186,71 @@ int check_backward(const void* Q, const void* K, const void* V, const float* Ome
   return FAVOR_OK;
 }
 
+// Scratch of favor_attention_noalloc: one fixed array per device.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device (with that device current)
+// and only that address is passed to kernels.
+__device__ __align__(256) unsigned char scratch[FAVOR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_device(hipStream_t s, int* dev) {
+  if (s) return hipStreamGetDevice(s, dev) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  return hipGetDevice(dev) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+// Device address of `scratch` on device dev, looked up on the first call
+// for that device.
+int scratch_address(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return FAVOR_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FAVOR_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FAVOR_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return FAVOR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FAVOR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int favor_attention_noalloc(const void* Q, const void* K, const void* V, const float* Omega,
+                            void* out, int B, int H, int L, int d, int m, int dtype, int kind,
+                            int causal, void* stream, int path) {
+  // argument and size checks before the device is touched
+  Problem p;
+  bool empty;
+  int st = check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty);
+  if (st != FAVOR_OK) return st;
+  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (empty) return FAVOR_OK;
+  if (!Q || !K || !V || !Omega || !out) return FAVOR_ERR_INVALID_ARG;
+  const int r = resolve(p, path);
+  if (r < 0) return r;
+  if (ws_bytes(p, r) > FAVOR_NOALLOC_SCRATCH_BYTES) return FAVOR_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = -1;
+  st = noalloc_device(s, &dev);
+  if (st != FAVOR_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(dev, &ws);
+  if (st != FAVOR_OK) return st;
+  Checked c;
+  st = check_call(Q, K, V, Omega, out, B, H, L, d, m, dtype, kind, causal, ws,
+                  FAVOR_NOALLOC_SCRATCH_BYTES, path, &c);
+  if (st != FAVOR_OK || c.empty) return st;
+  return launch(c, Q, K, V, Omega, out, ws, FAVOR_NOALLOC_SCRATCH_BYTES, s, nullptr);
+}
 
 int favor_version(void) { return kVersion; }
 

@@ -259,3 +259,24 @@ def test_backward_workspace_covers_forward_state():
     # outside the MFMA family (float32, or d != 64) the generic kernels run
     assert F.favor_attention_backward_workspace_bytes(1, 8, 4096, 64, 256, "f32", "trig", True, "mfma") == 0
     assert F.favor_attention_backward_resolve_path(1, 8, 4096, 32, 256, "bf16", "trig", True) == "generic"
+
+
+def noalloc(q=QA, k=KA, v=VA, w=WA, o=OA, B_=2, H=2, L=64, d=64, m=256, dt=1, kind=0, causal=0,
+            path=0):
+    return F.lib().favor_attention_noalloc(q, k, v, w, o, B_, H, L, d, m, dt, kind, causal, None,
+                                           path)
+
+
+def test_noalloc_host_checks():
+    # the entry point without a workspace argument checks its arguments and
+    # its scratch limit before it touches a device
+    assert noalloc(q=0) == B.FAVOR_ERR_INVALID_ARG
+    assert noalloc(dt=3) == B.FAVOR_ERR_INVALID_ARG
+    assert noalloc(path=7) == B.FAVOR_ERR_INVALID_ARG
+    assert noalloc(d=128) == B.FAVOR_ERR_UNSUPPORTED
+    for kw in (dict(L=0), dict(B_=0)):
+        assert noalloc(q=0, k=0, v=0, w=0, o=0, **kw) == B.FAVOR_OK
+    # beyond FAVOR_NOALLOC_SCRATCH_BYTES (64 MiB): rejected, nothing enqueued
+    big = dict(B_=64, H=8, L=32768, causal=1)
+    assert F.favor_attention_workspace_bytes(64, 8, 32768, 64, 256, "bf16", "trig", True) > 64 << 20
+    assert noalloc(**big) == B.FAVOR_ERR_WORKSPACE
