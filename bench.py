@@ -285,7 +285,7 @@ def main():
     # about 13 % slow on the headline shape), then a long timed block
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--path", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--path", default="auto", choices=["auto", "generic", "mfma", "small"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -317,6 +317,9 @@ def main():
         from linear_kernelized_attention_amd import sweep
         print(json.dumps(sweep.run()), flush=True)
         return
+    if args.calibrate_copy:
+        nbytes = calibrate_copy()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes}), flush=True)
     if args.only:
         key = args.only
         if key == "block":
@@ -334,10 +337,6 @@ def main():
             rec = {"only": key, "us_per_call": sec * 1e6, "path": rp, "phases_ms": {n: t for n, t in ph}}
         print(json.dumps(rec), flush=True)
         return
-    if args.calibrate_copy:
-        nbytes = calibrate_copy()
-        print(json.dumps({"copy_calibration_bytes_read": nbytes}), flush=True)
-
     # The other workloads run first: they are timed for the record's
     # "extra" field, and they leave the GPU at its steady-state clocks
     # before the headline's warm-up and timed steps.

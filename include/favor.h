@@ -76,9 +76,17 @@ typedef enum {
 
 /* Kernel family selection for favor_attention_ex (AUTO = the fastest path
  * that supports the request).  MFMA requires bf16, d = 64 and m a multiple
- * of 32 with m <= 256, or m = 512 for the bidirectional forward; GENERIC
- * handles f32 and bf16 with d <= 64. */
-typedef enum { FAVOR_PATH_AUTO = 0, FAVOR_PATH_GENERIC = 1, FAVOR_PATH_MFMA = 2 } favor_path;
+ * of 32 with m <= 256, or m = 512 for the bidirectional forward; SMALL (the
+ * forward of small bidirectional problems in two launches, float32
+ * arithmetic) requires d <= 32, m <= 128 and L <= 1024; GENERIC handles f32
+ * and bf16 with d <= 64.  AUTO tries them in that order.  The backward pass
+ * has MFMA and GENERIC families (SMALL returns FAVOR_ERR_UNSUPPORTED). */
+typedef enum {
+  FAVOR_PATH_AUTO = 0,
+  FAVOR_PATH_GENERIC = 1,
+  FAVOR_PATH_MFMA = 2,
+  FAVOR_PATH_SMALL = 3
+} favor_path;
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
 int favor_version(void);
@@ -180,8 +188,9 @@ int favor_attention_train(const void* Q, const void* K, const void* V, const flo
                           int causal, void* workspace, size_t workspace_bytes, void* stream,
                           int path);
 
-/* The favor_path that favor_attention_ex(..., path) would run (GENERIC or
- * MFMA), or a negative favor_status if the request is invalid/unsupported. */
+/* The favor_path that favor_attention_ex(..., path) would run (GENERIC,
+ * MFMA or SMALL), or a negative favor_status if the request is
+ * invalid/unsupported. */
 int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, int kind,
                                  int causal, int path);
 

@@ -48,20 +48,28 @@ int resolve(const Problem& p, int path) {
   switch (path) {
     case FAVOR_PATH_AUTO:
       if (favor::mfma::supports(p)) return FAVOR_PATH_MFMA;
+      if (favor::small::supports(p)) return FAVOR_PATH_SMALL;
       if (favor::generic::supports(p)) return FAVOR_PATH_GENERIC;
       return FAVOR_ERR_UNSUPPORTED;
     case FAVOR_PATH_GENERIC:
       return favor::generic::supports(p) ? FAVOR_PATH_GENERIC : FAVOR_ERR_UNSUPPORTED;
     case FAVOR_PATH_MFMA:
       return favor::mfma::supports(p) ? FAVOR_PATH_MFMA : FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_SMALL:
+      return favor::small::supports(p) ? FAVOR_PATH_SMALL : FAVOR_ERR_UNSUPPORTED;
     default:
       return FAVOR_ERR_INVALID_ARG;
   }
 }
 
+bool valid_path(int path) { return path >= FAVOR_PATH_AUTO && path <= FAVOR_PATH_SMALL; }
+
 size_t ws_bytes(const Problem& p, int resolved) {
-  return resolved == FAVOR_PATH_MFMA ? favor::mfma::workspace_bytes(p)
-                                     : favor::generic::workspace_bytes(p);
+  switch (resolved) {
+    case FAVOR_PATH_MFMA: return favor::mfma::workspace_bytes(p);
+    case FAVOR_PATH_SMALL: return favor::small::workspace_bytes(p);
+    default: return favor::generic::workspace_bytes(p);
+  }
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -83,7 +91,7 @@ int check_call(const void* Q, const void* K, const void* V, const float* Omega, 
                size_t ws_bytes_given, int path, Checked* c) {
   int st = check_problem(B, H, L, d, m, dtype, kind, causal, &c->p, &c->empty);
   if (st != FAVOR_OK) return st;
-  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_path(path)) return FAVOR_ERR_INVALID_ARG;
   if (c->empty) {
     c->path = FAVOR_PATH_GENERIC;
     return FAVOR_OK;
@@ -114,8 +122,9 @@ int launch(const Checked& c, const void* Q, const void* K, const void* V, const 
            void* out, void* ws, size_t wsb, hipStream_t s, favor::PhaseHook* hook,
            float* den = nullptr) {
   favor::Buffers b{Q, K, V, Omega, out, ws, wsb, den};
-  hipError_t e = c.path == FAVOR_PATH_MFMA ? favor::mfma::run(c.p, b, s, hook)
-                                           : favor::generic::run(c.p, b, s, hook);
+  hipError_t e = c.path == FAVOR_PATH_MFMA    ? favor::mfma::run(c.p, b, s, hook)
+                 : c.path == FAVOR_PATH_SMALL ? favor::small::run(c.p, b, s, hook)
+                                              : favor::generic::run(c.p, b, s, hook);
   if (e != hipSuccess) return FAVOR_ERR_HIP;
   if (hipPeekAtLastError() != hipSuccess) {
     (void)hipGetLastError();
@@ -136,6 +145,8 @@ int resolve_backward(const Problem& p, int path) {
       return favor::generic::supports(p) ? FAVOR_PATH_GENERIC : FAVOR_ERR_UNSUPPORTED;
     case FAVOR_PATH_MFMA:
       return favor::mfma::supports_backward(p) ? FAVOR_PATH_MFMA : FAVOR_ERR_UNSUPPORTED;
+    case FAVOR_PATH_SMALL:
+      return FAVOR_ERR_UNSUPPORTED;   // no backward kernels in this family
     default:
       return FAVOR_ERR_INVALID_ARG;
   }
@@ -152,7 +163,7 @@ int check_backward(const void* Q, const void* K, const void* V, const float* Ome
                    int path, Checked* c) {
   int st = check_problem(B, H, L, d, m, dtype, kind, causal, &c->p, &c->empty);
   if (st != FAVOR_OK) return st;
-  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_path(path)) return FAVOR_ERR_INVALID_ARG;
   c->path = FAVOR_PATH_GENERIC;
   if (c->empty) return FAVOR_OK;
   if (!Q || !K || !V || !Omega || !dOut || !dQ || !dK || !dV) return FAVOR_ERR_INVALID_ARG;
@@ -232,7 +243,7 @@ int favor_attention_noalloc(const void* Q, const void* K, const void* V, const f
   bool empty;
   int st = check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty);
   if (st != FAVOR_OK) return st;
-  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_path(path)) return FAVOR_ERR_INVALID_ARG;
   if (empty) return FAVOR_OK;
   if (!Q || !K || !V || !Omega || !out) return FAVOR_ERR_INVALID_ARG;
   const int r = resolve(p, path);
@@ -314,7 +325,7 @@ int favor_attention_resolve_path(int B, int H, int L, int d, int m, int dtype, i
   bool empty;
   int st = check_problem(B, H, L, d, m, dtype, kind, causal, &p, &empty);
   if (st != FAVOR_OK) return st;
-  if (path < FAVOR_PATH_AUTO || path > FAVOR_PATH_MFMA) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_path(path)) return FAVOR_ERR_INVALID_ARG;
   return resolve(p, path);
 }
 

@@ -10,7 +10,7 @@ namespace favor {
 
 enum { KIND_TRIG = 0, KIND_RELU = 1, KIND_POS = 2 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
-enum { PATH_AUTO = 0, PATH_GENERIC = 1, PATH_MFMA = 2 };
+enum { PATH_AUTO = 0, PATH_GENERIC = 1, PATH_MFMA = 2, PATH_SMALL = 3 };
 
 struct Problem {
   int B, H, L, d, m, dtype, kind, causal;
@@ -86,6 +86,14 @@ size_t backward_workspace_bytes(const Problem& p);
 hipError_t run_backward(const Problem& p, const Buffers& b, const BwdBuffers& g, hipStream_t s,
                         PhaseHook* hook);
 }  // namespace generic
+
+// small bidirectional problems: two launches, float32 arithmetic
+// (small_kernels.hip)
+namespace small {
+bool supports(const Problem& p);
+size_t workspace_bytes(const Problem& p);
+hipError_t run(const Problem& p, const Buffers& b, hipStream_t s, PhaseHook* hook);
+}  // namespace small
 
 namespace mfma {
 bool supports(const Problem& p);

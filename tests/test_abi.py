@@ -117,10 +117,23 @@ def test_workspace_sizes_monotone():
 
 
 def test_resolve_path():
-    assert F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False) == "generic"
-    assert F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False, "generic") == "generic"
+    # the small float32 workload runs on the two-launch small path; the
+    # generic kernels take it when asked, MFMA cannot
+    R = F.favor_attention_resolve_path
+    assert R(1, 1, 512, 16, 64, "f32", "trig", False) == "small"
+    assert R(1, 1, 512, 16, 64, "f32", "trig", False, "generic") == "generic"
+    assert R(1, 1, 512, 16, 64, "f32", "trig", False, "small") == "small"
     with pytest.raises(F.FavorError):
-        F.favor_attention_resolve_path(1, 1, 512, 16, 64, "f32", "trig", False, "mfma")
+        R(1, 1, 512, 16, 64, "f32", "trig", False, "mfma")
+    # the small path: bidirectional, d <= 32, m <= 128, L <= 1024
+    for args in ((1, 1, 512, 16, 64, "f32", "trig", True), (1, 1, 512, 64, 64, "f32", "trig", False),
+                 (1, 1, 512, 16, 256, "f32", "trig", False), (1, 1, 2048, 16, 64, "f32", "trig", False)):
+        assert R(*args) == "generic"
+        with pytest.raises(F.FavorError):
+            R(*args, "small")
+    assert R(2, 4, 1024, 32, 128, "bf16", "relu", False) == "small"
+    # no backward kernels in the small family
+    assert F.favor_attention_backward_workspace_bytes(1, 1, 512, 16, 64, "f32", "trig", False, "small") == 0
 
 
 @pytest.mark.parametrize("kind", ["trig", "relu", "positive"])

@@ -19,8 +19,12 @@ pytestmark = pytest.mark.gpu
 
 def _paths(B, H, L, d, m, dtype, kind, causal):
     paths = ["generic"]
-    if F.favor_attention_resolve_path(B, H, L, d, m, dtype, kind, causal) == "mfma":
-        paths.append("mfma")
+    for fam in ("mfma", "small"):
+        try:
+            F.favor_attention_resolve_path(B, H, L, d, m, dtype, kind, causal, fam)
+            paths.append(fam)
+        except F.FavorError:
+            pass
     return paths
 
 

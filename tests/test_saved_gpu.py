@@ -35,6 +35,18 @@ def _paths(shape, kind, causal):
     return paths
 
 
+def _fwd_paths(shape, kind, causal):
+    # the forward families, the small two-launch path included
+    B, H, L, d, m, dtype = shape
+    paths = _paths(shape, kind, causal)
+    try:
+        F.favor_attention_resolve_path(B, H, L, d, m, dtype, kind, causal, "small")
+        paths.append("small")
+    except F.FavorError:
+        pass
+    return paths
+
+
 def _oracle_den(q, k, W, kind, causal):
     """sum_j phi(q_i) . phi(k_j) over j (j <= i when causal), per (b, h)."""
     pq, pk = O.feature_map(q, W, kind), O.feature_map(k, W, kind)
@@ -60,7 +72,7 @@ def test_forward_den(shape, kind, causal):
         out_ref = O.favor_attention(q, k, v, W, kind, causal)
     if not np.isfinite(out_ref).all():
         pytest.skip("0/0 row in the forward (ReLU)")
-    for path in _paths(shape, kind, causal):
+    for path in _fwd_paths(shape, kind, causal):
         out, den = F.favor_attention(*dev, kind=kind, causal=causal, path=path, den=True)
         plain = F.favor_attention(*dev, kind=kind, causal=causal, path=path)
         torch.cuda.synchronize()
