@@ -86,9 +86,10 @@ def sources_sha256(names):
     return h.hexdigest() if names else None
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; otherwise None."""
+def load_traffic(kernel: str, workload: str = "head"):
+    """HBM bytes per launch of a kernel (phase name) of a workload, from the
+    committed rocprofv3 counter runs, if they were taken on the current
+    kernel source; otherwise None."""
     fn = os.path.join(PROFILE_DIR, "traffic.json")
     if not os.path.exists(fn):
         return None
@@ -96,12 +97,24 @@ def load_traffic(kernel: str):
         rec = json.load(open(fn))
     except (OSError, ValueError):
         return None
-    ent = rec.get("kernels", {}).get(kernel)
+    ent = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     if not ent:
         return None
     if sources_sha256(ent.get("sources", [])) != ent.get("sources_sha256"):
         return None
     return float(ent["bytes_per_launch"])
+
+
+def counter_bytes_per_call(workload: str, phases):
+    """HBM bytes of one call from the counter runs (every phase of the call
+    must have a current entry), or None."""
+    total = 0.0
+    for name, _ in phases:
+        b = load_traffic(name, workload)
+        if b is None:
+            return None
+        total += b
+    return total
 
 
 def upload_one(x, dtype):
@@ -353,6 +366,12 @@ def main():
                           "path": rp, "mfma_frac": fl / s / 1e12 / PEAK_BF16_MFMA_TFLOPS,
                           "hbm_frac": by / s / 1e9 / PEAK_HBM_GBS,
                           "phases_ms": {n: t for n, t in ph}}
+            # HBM bytes actually moved (FETCH_SIZE + WRITE_SIZE counters),
+            # the state streaming of the causal path included
+            cb = counter_bytes_per_call(key, ph)
+            if cb is not None:
+                extra[key]["hbm_counter_bytes_per_call"] = cb
+                extra[key]["hbm_counter_frac"] = cb / s / 1e9 / PEAK_HBM_GBS
         sb = bench_block(F, I, steps, 3)
         cfg = I.BLOCK_WORKLOAD
         sf = bench_random(F, (cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["m"]), cfg["kind"], False,
