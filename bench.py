@@ -40,6 +40,10 @@ UNIT = "tokens*heads/s"
 PEAK_BF16_MFMA_TFLOPS = 2516.6   # dense, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3
+# untimed back-to-back calls before each other workload is timed, so that
+# each is measured at the loaded clock and the last of them leaves the GPU
+# there for the headline's warm-up and timed steps
+EXTRA_SETTLE_S = 0.03
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -128,8 +132,23 @@ def upload(ai, dtype):
     return [upload_one(x, dtype) for x in (ai.q, ai.k, ai.v)]
 
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps, warmup, settle=0.0):
+    """Seconds per call over `steps` timed calls after `warmup` untimed ones.
+    With settle > 0, untimed calls first run back to back for that many
+    seconds: the GPU raises its clocks over about 20 ms of continuous work
+    (measured on the headline: 54 us per call at first, 44.5 us after
+    400 calls) and drops them again when idle."""
     import torch
+    if settle > 0:
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= settle:
+                    break
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -140,7 +159,12 @@ def time_calls(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def bench_attention(F, I, w, steps, warmup, path="auto"):
+def prep_attention(F, I, w, path="auto"):
+    """Uploads a workload's seeded inputs; returns run(steps, warmup) ->
+    (seconds per favor_attention call, per-kernel phases, resolved path).
+    Inputs are made before any timing starts, so that the timed blocks run
+    back to back and the GPU does not idle (and drop its clocks) while the
+    host draws the next workload's inputs."""
     import torch
     ai, dr = I.workload_inputs(w)
     q, k, v = upload(ai, w.dtype)
@@ -150,14 +174,19 @@ def bench_attention(F, I, w, steps, warmup, path="auto"):
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     fn = lambda: F.favor_attention(q, k, v, omega, kind=w.kind, causal=w.causal, path=path, out=out,
                                    workspace=ws)
-    sec = time_calls(fn, steps, warmup)
-    phases = F.favor_profile_attention(q, k, v, omega, kind=w.kind, causal=w.causal, path=path,
-                                       iters=max(steps, 20), out=out, workspace=ws)
-    resolved = F.favor_attention_resolve_path(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal, path)
-    return sec, phases, resolved
+
+    def run(steps, warmup, settle=0.0):
+        sec = time_calls(fn, steps, warmup, settle)
+        phases = F.favor_profile_attention(q, k, v, omega, kind=w.kind, causal=w.causal, path=path,
+                                           iters=max(steps, 20), out=out, workspace=ws)
+        resolved = F.favor_attention_resolve_path(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind,
+                                                  w.causal, path)
+        return sec, phases, resolved
+    return run
 
 
-def bench_block(F, I, steps, warmup):
+def prep_block(F, I):
+    """run(steps, warmup) -> seconds per masked-LM block call."""
     import torch
     cfg = I.BLOCK_WORKLOAD
     b = I.block_inputs(B=cfg["B"], L=cfg["L"], E=cfg["E"], H=cfg["H"], seed=0)
@@ -168,11 +197,11 @@ def bench_block(F, I, steps, warmup):
     ids = torch.from_numpy(b.ids).cuda()
     weights = F.favor_block_weights(*dev[1:])   # packed once, as at model load
     fn = lambda: F.favor_performer_block(ids, dev[0], weights, omega, heads=cfg["H"], kind=cfg["kind"])
-    return time_calls(fn, steps, warmup)
+    return lambda steps, warmup, settle=0.0: time_calls(fn, steps, warmup, settle)
 
 
-def bench_backward(F, I, w, steps, warmup, saved=False):
-    """Seconds per favor_attention_backward call on a workload's seeded
+def prep_backward(F, I, w, saved=False):
+    """run(steps, warmup) -> seconds per favor_attention_backward call on a workload's seeded
     inputs and a seeded N(0, 1) output gradient; with saved, the forward's
     (out, den) from favor_attention(..., den=True), made once before timing,
     is passed in (the training pattern)."""
@@ -189,7 +218,7 @@ def bench_backward(F, I, w, steps, warmup, saved=False):
     sv = F.favor_attention(q, k, v, omega, kind=w.kind, causal=w.causal, den=True) if saved else None
     fn = lambda: F.favor_attention_backward(q, k, v, omega, g, kind=w.kind, causal=w.causal,
                                             workspace=ws, grads=grads, saved=sv)
-    return time_calls(fn, steps, warmup)
+    return lambda steps, warmup, settle=0.0: time_calls(fn, steps, warmup, settle)
 
 
 def backward_work(B, H, L, d, m, kind):
@@ -201,8 +230,8 @@ def backward_work(B, H, L, d, m, kind):
     return B * H * L * (8 * d * m + 12 * F_ * (d + 1))
 
 
-def bench_random(F, shape, kind, causal, steps, warmup):
-    """Seconds per favor_attention call on random bf16 inputs of a shape
+def prep_random(F, shape, kind, causal):
+    """run(steps, warmup) -> seconds per favor_attention call on random bf16 inputs of a shape
     (timing only: values N(0,1) d^-1/4 drawn on the device, Omega from the
     seeded orthogonal draw)."""
     import torch
@@ -217,7 +246,7 @@ def bench_random(F, shape, kind, causal, steps, warmup):
     need = F.favor_attention_workspace_bytes(B, H, L, d, m, "bf16", kind, causal, "auto")
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     fn = lambda: F.favor_attention(q, k, v, omega, kind=kind, causal=causal, out=out, workspace=ws)
-    return time_calls(fn, steps, warmup)
+    return lambda steps, warmup, settle=0.0: time_calls(fn, steps, warmup, settle)
 
 
 def cpu_oracle_once(I, w):
@@ -336,31 +365,47 @@ def main():
     if args.only:
         key = args.only
         if key == "block":
-            sec = bench_block(F, I, args.steps, args.warmup)
+            sec = prep_block(F, I)(args.steps, args.warmup)
             rec = {"only": key, "us_per_call": sec * 1e6}
         elif key.startswith("bwd_") or key.startswith("bwds_"):
             saved = key.startswith("bwds_")
             wk = I.WORKLOADS[key.split("_", 1)[1]]
-            sec = bench_backward(F, I, wk, args.steps, args.warmup, saved)
+            sec = prep_backward(F, I, wk, saved)(args.steps, args.warmup)
             rec = {"only": key, "us_per_call": sec * 1e6,
                    "algorithmic_tflops": backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind) / sec / 1e12}
         else:
             wk = I.WORKLOADS[key]
-            sec, ph, rp = bench_attention(F, I, wk, args.steps, args.warmup, args.path)
+            sec, ph, rp = prep_attention(F, I, wk, args.path)(args.steps, args.warmup)
             rec = {"only": key, "us_per_call": sec * 1e6, "path": rp, "phases_ms": {n: t for n, t in ph}}
         print(json.dumps(rec), flush=True)
         return
-    # The other workloads run first: they are timed for the record's
-    # "extra" field, and they leave the GPU at its steady-state clocks
-    # before the headline's warm-up and timed steps.
-    extra = None
+    # Every workload's inputs are drawn and uploaded before the first timed
+    # block; the other workloads then run first, back to back, for the
+    # record's "extra" field, which leaves the GPU at its steady-state
+    # clocks for the headline's warm-up and timed steps that follow.
     w = I.WORKLOADS["head"]
+    head_run = prep_attention(F, I, w, args.path)
+    extra = None
     if not args.no_extra:
+        fwd_keys = ("c3_causal", "c2_trig", "c2_relu", "c4_bidir", "c4_causal", "c1", "pos_bidir",
+                    "pos_causal")
+        bwd_keys = (("head", False), ("c3_causal", False), ("c2_trig", False), ("head", True),
+                    ("c3_causal", True))
+        cfg = I.BLOCK_WORKLOAD
+        fwd_runs = {key: prep_attention(F, I, I.WORKLOADS[key], "auto") for key in fwd_keys}
+        block_run = prep_block(F, I)
+        block_favor_run = prep_random(F, (cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["m"]),
+                                      cfg["kind"], False)
+        bwd_runs = {(key, saved): prep_backward(F, I, I.WORKLOADS[key], saved) for key, saved in bwd_keys}
+        sweep_runs = {Bs: prep_random(F, (Bs, w.H, w.L, w.d, w.m), w.kind, w.causal) for Bs in (8, 16, 32)}
+        torch.cuda.synchronize()
+
         extra = {}
         steps = max(10, args.steps // 4)
-        for key in ("c3_causal", "c2_trig", "c2_relu", "c4_bidir", "c4_causal", "c1", "pos_bidir", "pos_causal"):
+        settle = EXTRA_SETTLE_S
+        for key in fwd_keys:
             wk = I.WORKLOADS[key]
-            s, ph, rp = bench_attention(F, I, wk, steps, max(3, args.warmup // 4), "auto")
+            s, ph, rp = fwd_runs[key](steps, max(3, args.warmup // 4), settle)
             fl, by = path_total_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind, 4 if wk.dtype == "f32" else 2)
             extra[key] = {"us_per_call": s * 1e6, "tokens_x_heads_per_s": wk.tokens_x_heads / s,
                           "path": rp, "mfma_frac": fl / s / 1e12 / PEAK_BF16_MFMA_TFLOPS,
@@ -372,18 +417,15 @@ def main():
             if cb is not None:
                 extra[key]["hbm_counter_bytes_per_call"] = cb
                 extra[key]["hbm_counter_frac"] = cb / s / 1e9 / PEAK_HBM_GBS
-        sb = bench_block(F, I, steps, 3)
-        cfg = I.BLOCK_WORKLOAD
-        sf = bench_random(F, (cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["m"]), cfg["kind"], False,
-                          steps, 3)
+        sb = block_run(steps, 3, settle)
+        sf = block_favor_run(steps, 3, settle)
         extra["c5_block"] = {"us_per_call": sb * 1e6, "tokens_per_s": cfg["B"] * cfg["L"] / sb,
                              "favor_us_per_call": sf * 1e6}
         # backward pass on the headline, causal and B8 H8 L1024 shapes, and
         # (bwds_) with the forward's saved output and row normalisers
-        for key, saved in (("head", False), ("c3_causal", False), ("c2_trig", False),
-                           ("head", True), ("c3_causal", True)):
+        for key, saved in bwd_keys:
             wk = I.WORKLOADS[key]
-            sbw = bench_backward(F, I, wk, steps, max(3, args.warmup // 4), saved)
+            sbw = bwd_runs[(key, saved)](steps, max(3, args.warmup // 4), settle)
             fl = backward_work(wk.B, wk.H, wk.L, wk.d, wk.m, wk.kind)
             rp = F.favor_attention_backward_resolve_path(wk.B, wk.H, wk.L, wk.d, wk.m, wk.dtype,
                                                          wk.kind, wk.causal)
@@ -394,14 +436,14 @@ def main():
                                    "peak": "bf16 MFMA" if rp == "mfma" else "fp32 VALU"}
         # saturation: the headline shape at larger batch (timing on random inputs)
         sweep = {}
-        for Bs in (8, 16, 32):
-            ss = bench_random(F, (Bs, w.H, w.L, w.d, w.m), w.kind, w.causal, steps, 3)
+        for Bs, run in sweep_runs.items():
+            ss = run(steps, 3, settle)
             fl, _ = path_total_work(Bs, w.H, w.L, w.d, w.m, w.kind)
             sweep[f"B{Bs}"] = {"us_per_call": ss * 1e6, "tokens_x_heads_per_s": Bs * w.H * w.L / ss,
                                "mfma_frac": fl / ss / 1e12 / PEAK_BF16_MFMA_TFLOPS}
         extra["head_sweep"] = sweep
 
-    sec, phases, resolved = bench_attention(F, I, w, args.steps, args.warmup, args.path)
+    sec, phases, resolved = head_run(args.steps, args.warmup)
     value = w.tokens_x_heads / sec
 
     # dominant kernel: the longest phase of one call
