@@ -529,6 +529,10 @@ CausalPlan plan_causal(const Problem& p) {
   const int n_fpart = p.m / rows;
   // one causal block per (head, segment); about 256 of them
   cp.keys = plan_keys(p, 256LL * n_fpart, TK);
+  // the key pass takes n_fpart segments per block (one partial each), so
+  // that it too runs about 256 blocks, each over as many tokens as a
+  // bidirectional key block
+  cp.keys.per_kv = n_fpart;
   cp.start_bytes = align_up((size_t)cp.keys.n_split * p.BH * state_elems(p.F) * sizeof(uint16_t), 256);
   return cp;
 }

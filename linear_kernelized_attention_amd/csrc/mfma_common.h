@@ -166,8 +166,11 @@ __device__ inline float sixteen_sum(float x) {
 
 // One key task = (head bh, token split, feature part), run by one block of
 // NW waves; wave w owns the 16 Omega rows r0 = part * 16 NW + 16 w .. +15.
-// Writes its tiles of the bf16 partial state of (split, head) (trig: sin
-// features r, cos features M + r) in the state layout, 8 bytes per lane.
+// Writes its tiles of the bf16 partial states of the split's tokens (trig:
+// sin features r, cos features M + r) in the state layout, 8 bytes per
+// lane: one partial per out_len tokens (out_len divides seg_len and is a
+// multiple of the key tile), partial j of split s at index
+// s * (seg_len / out_len) + j, for indices below n_out.
 //
 // The key tiles stream through three LDS buffers (tile i in buffer i % 3).
 // Each tile is four steps of 32 tokens, software-pipelined across steps and
@@ -190,7 +193,7 @@ template <int KIND, int NW, bool ZSRC = false>
 __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                       const float* __restrict__ Omega, uint16_t* __restrict__ part,
                                       uint16_t* __restrict__ ofrag, int L, int M, int n_fpart,
-                                      int seg_len, long long BH,
+                                      int seg_len, int out_len, int n_out, long long BH,
                                       float omega_scale, float knorm_scale, long long bh, int task,
                                       uint16_t* lds, const float* __restrict__ zsrc = nullptr) {
   constexpr bool TRIG = KIND == KIND_TRIG;
@@ -360,6 +363,26 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       for (int f = 0; f < FT; ++f) acc[f][n] = mfma16(fa[f], vf[n], acc[f][n]);
   };
 
+  // the partial of the out_len tokens that tile i belongs to
+  const int per_split = seg_len / out_len;
+  auto write_part = [&](int i) {
+    const int pidx = split * per_split + i * TK / out_len;
+    if (pidx >= n_out) return;
+    uint16_t* P0 = part + ((size_t)pidx * BH + bh) * state_elems(F);
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      const int ft = (f * M + r0) / 16;
+#pragma unroll
+      for (int n = 0; n < 5; ++n) {
+        u32x2 o;
+        o[0] = pack2(acc[f][n][0], acc[f][n][1]);
+        o[1] = pack2(acc[f][n][2], acc[f][n][3]);
+        if (n < 4) *(u32x2*)(P0 + vtile_off(ft, n) + lane * 4) = o;
+        else if (c == 0) *(u32x2*)(P0 + z_off(F, 16 * ft + 4 * g)) = o;   // column 64: z
+      }
+    }
+  };
+
   // prologue: load tiles 0 and 1 together, stage them, load tile 2,
   // project step 0
   using B0 = std::integral_constant<int, 0>;
@@ -406,6 +429,15 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
       if (POS) ld_h(Hn[B], s, hv);
       ld_k(s < 2 ? ksc : ksn, (s + 2) & 3, k2);
       contr(fprev, vprev);
+      // tile i starts a new partial: the contraction just issued was the
+      // last step of the previous one
+      if (s == 0 && per_split > 1 && i > 0 && (i * TK) % out_len == 0) {
+        write_part(i - 1);
+#pragma unroll
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+          for (int n = 0; n < 5; ++n) acc[f][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
       proj(kn, Pn);
       feat(P, hv, fcur);
       if (s == 1) {
@@ -438,19 +470,7 @@ __device__ inline void kv_state_block(const uint16_t* __restrict__ K, const uint
   }
   contr(fprev, vprev);
 
-  uint16_t* P0 = part + ((size_t)split * BH + bh) * state_elems(F);
-#pragma unroll
-  for (int f = 0; f < FT; ++f) {
-    const int ft = (f * M + r0) / 16;
-#pragma unroll
-    for (int n = 0; n < 5; ++n) {
-      u32x2 o;
-      o[0] = pack2(acc[f][n][0], acc[f][n][1]);
-      o[1] = pack2(acc[f][n][2], acc[f][n][3]);
-      if (n < 4) *(u32x2*)(P0 + vtile_off(ft, n) + lane * 4) = o;
-      else if (c == 0) *(u32x2*)(P0 + z_off(F, 16 * ft + 4 * g)) = o;   // column 64: z
-    }
-  }
+  write_part(n_tiles - 1);
 }
 
 // Standalone key-side kernel: one task per block, blocks numbered so that
@@ -462,13 +482,15 @@ __global__ __launch_bounds__(NW * 64) void kv_state_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ part,
                                                            uint16_t* __restrict__ ofrag, int L,
                                                            int M, int n_fpart, int seg_len,
+                                                           int out_len, int n_out,
                                                            long long BH, float omega_scale,
                                                            float knorm_scale,
                                                            const float* __restrict__ zsrc) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[KV_LDS_BYTES / sizeof(uint16_t)];
   const int nx = (int)((long long)gridDim.x / BH);   // blocks per head
   const long long lb = xcd_logical(blockIdx.x, gridDim.x);
-  kv_state_block<KIND, NW, ZSRC>(K, V, Omega, part, ofrag, L, M, n_fpart, seg_len, BH, omega_scale,
+  kv_state_block<KIND, NW, ZSRC>(K, V, Omega, part, ofrag, L, M, n_fpart, seg_len, out_len, n_out,
+                                 BH, omega_scale,
                                  knorm_scale, lb / nx, (int)(lb % nx), lds, zsrc);
 }
 
@@ -483,8 +505,11 @@ inline float omega_scale_for(int kind) {
 }
 
 // Key-side partition: token splits (segments) x feature parts per head.
+// A kv block covers kv_len = seg_len * per_kv tokens and writes one partial
+// per segment of seg_len tokens.
 struct Plan {
-  int n_split, seg_len;   // token splits of the key side
+  int n_split, seg_len;   // token splits of the key side (one partial each)
+  int per_kv;             // segments per kv block
   int nw_kv, n_fpart;     // waves per kv block, feature parts per head
   size_t part_bytes;      // bf16 partial states [n_split][BH] in the state layout
   size_t ofrag_bytes;     // bf16 Omega~ A fragments [m / 16][2][64][8]
@@ -507,6 +532,7 @@ inline Plan plan_keys(const Problem& p, long long target_blocks, int seg_quantum
   seg = (seg + seg_quantum - 1) / seg_quantum * seg_quantum;
   pl.seg_len = (int)seg;
   pl.n_split = (int)((p.L + seg - 1) / seg);
+  pl.per_kv = 1;
   pl.part_bytes = align_up((size_t)pl.n_split * p.BH * state_elems(p.F) * sizeof(uint16_t), 256);
   pl.ofrag_bytes = align_up((size_t)(p.m / 16) * 2 * 512 * sizeof(uint16_t), 256);
   return pl;
@@ -521,10 +547,11 @@ inline dim3 head_grid(long long x, long long BH) {
 template <int KIND, int NW, bool ZSRC = false>
 inline void launch_kv(const Problem& p, const Buffers& b, const Plan& pl, uint16_t* ofrag,
                       hipStream_t s, float oscale, const float* zsrc = nullptr) {
-  hipLaunchKernelGGL((kv_state_kernel<KIND, NW, ZSRC>), dim3((unsigned)((long long)pl.n_split * pl.n_fpart * p.BH)),
+  const long long kv_splits = (pl.n_split + pl.per_kv - 1) / pl.per_kv;
+  hipLaunchKernelGGL((kv_state_kernel<KIND, NW, ZSRC>), dim3((unsigned)(kv_splits * pl.n_fpart * p.BH)),
                      dim3(NW * 64), 0, s, (const uint16_t*)b.k, (const uint16_t*)b.v, b.omega,
-                     (uint16_t*)b.ws, ofrag, p.L, p.m, pl.n_fpart, pl.seg_len, p.BH, oscale,
-                     1.0f / sqrtf((float)D), zsrc);
+                     (uint16_t*)b.ws, ofrag, p.L, p.m, pl.n_fpart, pl.seg_len * pl.per_kv,
+                     pl.seg_len, pl.n_split, p.BH, oscale, 1.0f / sqrtf((float)D), zsrc);
 }
 
 template <int KIND, bool ZSRC = false>
