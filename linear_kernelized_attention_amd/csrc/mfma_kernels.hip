@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const uint16_t* __restri
 // tokens), and the readout out^T += S^T phi^T.  The loop is fully unrolled
 // and software-pipelined: the feature map of pair i is independent of the
 // projection of pair i + 1 and the readout of pair i - 1.
-constexpr int RO_MAXSUM = 4;   // partial states the readout sums itself
+constexpr int RO_MAXSUM = 8;   // partial states the readout sums itself
 constexpr int OROW = D + 8;    // padded LDS row of the staged output
 
 template <int M, int F>
@@ -273,12 +273,12 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         const u32x4* src = (const u32x4*)(part + ((size_t)bh * FH + fh) * NS * 8);
         for (int i = tid; i < NS; i += NT) ((u32x4*)Sl)[i] = src[i];
       } else {
-        // nsum = 1..4, each a separately unrolled pass (no per-element
+        // nsum = 1..8, each a separately unrolled pass (no per-element
         // selects): all loads of a batch, then the float32 sums in split
         // order, starting from split 0
         auto pass = [&](auto ns_tag) {
           constexpr int NSUM = decltype(ns_tag)::value;
-          constexpr int BATCH = NSUM == 1 ? 10 : 20 / NSUM;
+          constexpr int BATCH = NSUM == 1 ? 10 : (20 / NSUM > 1 ? 20 / NSUM : 2);
           const Bf16HalfSel sel = bf16_half_selectors();
           for (int b0 = wv; b0 < NBLK; b0 += NW * BATCH) {
             u32x2 v[BATCH][2][NSUM];
@@ -327,7 +327,11 @@ __device__ inline void readout_block(const uint16_t* __restrict__ Q, const uint1
         if (nsum == 1) pass(std::integral_constant<int, 1>{});
         else if (nsum == 2) pass(std::integral_constant<int, 2>{});
         else if (nsum == 3) pass(std::integral_constant<int, 3>{});
-        else pass(std::integral_constant<int, 4>{});
+        else if (nsum == 4) pass(std::integral_constant<int, 4>{});
+        else if (nsum == 5) pass(std::integral_constant<int, 5>{});
+        else if (nsum == 6) pass(std::integral_constant<int, 6>{});
+        else if (nsum == 7) pass(std::integral_constant<int, 7>{});
+        else pass(std::integral_constant<int, 8>{});
       }
 #pragma unroll
       for (int k = 0; k < CO; ++k)

@@ -52,8 +52,10 @@ SMALL = [
     (2, 1, 70, 64, 32, "bf16"),
     # bidirectional MFMA readout summing 4 key-split partials (4 tiles of
     # 128 keys, the last ragged); 1 x 3 x 257 sums 3, 1 x 2 x 200 (m = 96)
-    # sums 2, and 1 x 1 x 1000 goes through the split-sum kernel
+    # sums 2, 1 x 1 x 1000 sums 8, and 1 x 1 x 1500 (12 splits) goes
+    # through the split-sum kernel
     (1, 2, 500, 64, 256, "bf16"),
+    (1, 1, 1500, 64, 256, "bf16"),
     # m = 512: the bidirectional MFMA readout in two feature passes (the
     # causal and float32 cases run on the generic kernels)
     (1, 2, 300, 64, 512, "bf16"),
