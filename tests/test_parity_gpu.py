@@ -12,7 +12,7 @@ import torch
 import linear_kernelized_attention_amd as F
 from linear_kernelized_attention_amd import inputs as I
 from oracle import favor_oracle as O
-from tests.gpu_util import TOL, assert_parity, from_device, problem, slice_rel_err
+from tests.gpu_util import TOL, assert_parity, from_device, problem, slice_rel_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -220,6 +220,55 @@ def test_causal_nonfinite_last_token_stays_local(which, kind):
             # (the device's ReLU features are max(P, 0) with IEEE maxNum: a
             # NaN projection gives the feature 0, so a NaN key drops out)
             assert torch.isnan(out[:, :, L - 1]).any(), path
+
+
+def _big_key_problem(norm, heads_with_big=(0, 1)):
+    # tokens 3, 100 and 257 of the given heads get keys of the given norm
+    B, H, L, d, m = 1, 2, 300, 64, 256
+    dev, (q, k, v), W = problem(B, H, L, d, m, "bf16", seed=11)
+    r = np.random.default_rng(11)
+    kb = k.copy()
+    for t in (3, 100, 257):
+        u = r.standard_normal((B, H, d))
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        for h in heads_with_big:
+            kb[:, h, t] = norm * u[:, h]
+    kst, k64 = I.to_storage(kb, "bf16")
+    return dev, (q, k64, v), W, to_device(kst, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("norm", [12.0, 30.0])
+def test_trig_large_key_norms(norm, causal):
+    # The trig key weight exp(|k~|^2 / 2) at d = 64: norm 30 gives
+    # exp(56.25), below the float32 limit exp(88.7); such keys dominate the
+    # rows that see them.  The bf16 projection's error grows with the key
+    # norm (about 1.6e-2 per row at norm 30); the float32 kernels stay at
+    # the bf16 output rounding.
+    dev, (q, k64, v), W, kd = _big_key_problem(norm)
+    ref = O.favor_attention(q, k64, v, W, "trig", causal)
+    for path in _paths(1, 2, 300, 64, 256, "bf16", "trig", causal):
+        got = F.favor_attention(dev[0], kd, dev[2], dev[3], kind="trig", causal=causal, path=path)
+        torch.cuda.synchronize()
+        assert_parity(from_device(got), ref, 2e-2, f"[{path}] key norm {norm} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_trig_key_weight_overflow(causal):
+    # Beyond |k~|^2 / 2 = 88.7 (norm 37.7 at d = 64) the float32 key weight
+    # overflows: the head with such keys has non-finite outputs (all of
+    # them when bidirectional), and the other head is unaffected.
+    dev, (q, k64, v), W, kd = _big_key_problem(40.0, heads_with_big=(0,))
+    ref = O.favor_attention(q, k64, v, W, "trig", causal)
+    for path in _paths(1, 2, 300, 64, 256, "bf16", "trig", causal):
+        got = from_device(F.favor_attention(dev[0], kd, dev[2], dev[3], kind="trig", causal=causal,
+                                            path=path))
+        torch.cuda.synchronize()
+        bad = ~np.isfinite(got[:, 0]).all(axis=-1)
+        assert bad[:, 3:].all(), path        # every row that sees token 3
+        if not causal:
+            assert bad.all(), path
+        assert_parity(got[:, 1:], ref[:, 1:], 2e-2, f"[{path}] head without large keys")
 
 
 def test_profile_reports_kernels():
