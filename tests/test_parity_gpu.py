@@ -271,6 +271,30 @@ def test_trig_key_weight_overflow(causal):
         assert_parity(got[:, 1:], ref[:, 1:], 2e-2, f"[{path}] head without large keys")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_more_heads_than_a_grid_dimension(dtype, d, causal):
+    # B * H = 66 000 heads: beyond 65 535, the kernels that take the head
+    # from the grid's y and z dimensions (and the MFMA ones, from a long x
+    # dimension) must still reach every head.  Heads around the boundary
+    # against the oracle, and bit for bit against the same heads run alone.
+    B, H, L, m = 2, 33000, 5, 32
+    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=21)
+    heads = [(0, 0), (1, 32534), (1, 32535), (1, 32999)]   # b * H + h = 0, 65534, 65535, 65999
+    for path in _paths(B, H, L, d, m, dtype, "trig", causal):
+        out = F.favor_attention(*dev, kind="trig", causal=causal, path=path)
+        torch.cuda.synchronize()
+        for b, h in heads:
+            one = F.favor_attention(*(x[b:b + 1, h:h + 1].contiguous() for x in dev[:3]), dev[3],
+                                    kind="trig", causal=causal, path=path)
+            torch.cuda.synchronize()
+            bits = torch.int16 if dtype == "bf16" else torch.int32
+            assert torch.equal(out[b, h].view(bits), one[0, 0].view(bits)), (path, b, h)
+            ref = O.favor_attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], W,
+                                    "trig", causal)
+            assert_parity(from_device(out[b:b + 1, h:h + 1]), ref, TOL[dtype], f"[{path}] head {b},{h}")
+
+
 def test_profile_reports_kernels():
     dev, _, _ = problem(1, 2, 512, 64, 256, "bf16")
     for path in _paths(1, 2, 512, 64, 256, "bf16", "trig", False):
