@@ -401,7 +401,7 @@ int favor_profile_attention(const void* Q, const void* K, const void* V, const f
     }
   }
   for (auto& e : ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
   if (rc != FAVOR_OK) return rc;
   for (int ph = 0; ph < phases; ++ph) phase_ms[ph] = (float)sum[ph];
   *n_phases = phases;

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NT) void readout_kernel(Args a) {
   const int qb = blockIdx.x;
   const long long bh = blockIdx.y + (long long)gridDim.y * blockIdx.z;
   if (bh >= a.BH) return;
-  const int tid = threadIdx.x, d = a.d, m = a.m, dp1 = d + 1;
+  const int tid = threadIdx.x, d = a.d, m = a.m;
   const bool trig = a.kind == KIND_TRIG;
   const int F = trig ? 2 * m : m;
   const long long t0 = (long long)qb * TQ;
