@@ -119,6 +119,12 @@ def test_backward_mfma_causal_many_segments():
     _check((1, 2, 8192, 64, 256, "bf16"), "trig", True, workers=O.default_workers(), paths=["mfma"])
 
 
+def test_backward_mfma_causal_segment_scan_remainder():
+    # 20 segments per head: the prefix and suffix scans run one batch of 16
+    # segments and four one at a time
+    _check((1, 2, 2560, 64, 256, "bf16"), "trig", True, workers=O.default_workers(), paths=["mfma"])
+
+
 def test_backward_config1():
     _check((1, 1, 512, 16, 64, "f32"), "trig", False)
 

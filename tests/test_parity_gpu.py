@@ -82,6 +82,18 @@ def test_small_full(shape, kind, causal):
         assert_parity(np.nan_to_num(got), ref_, TOL[dtype], f"[{path}] {shape} {kind} causal={causal}")
 
 
+@pytest.mark.parametrize("kind", ["trig", "positive"])
+def test_causal_segment_scan_batches(kind):
+    # B1 H2 L2560: 20 segments of 128 tokens per head on a grid of a few
+    # dozen blocks, so the exclusive segment scan runs one batch of 16
+    # segments and then four one at a time
+    B, H, L, d, m = 1, 2, 2560, 64, 256
+    dev, (q, k, v), W = problem(B, H, L, d, m, "bf16", seed=20)
+    ref = O.favor_attention(q, k, v, W, kind, True, workers=O.default_workers())
+    got = _run(dev, kind, True, "mfma")
+    assert_parity(got, ref, 2e-2, f"[mfma] {kind} causal, 20 segments")
+
+
 def test_config1_fp32():
     w = I.WORKLOADS["c1"]
     dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype)
