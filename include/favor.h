@@ -77,8 +77,12 @@ typedef enum {
 /* Kernel family selection for favor_attention_ex (AUTO = the fastest path
  * that supports the request).  MFMA requires bf16, d = 64 and m a multiple
  * of 32 with m <= 256, or m = 512 for the bidirectional forward; SMALL (the
- * forward of small bidirectional problems in two launches, float32
- * arithmetic) requires d <= 32, m <= 128 and L <= 1024; GENERIC handles f32
+ * forward of small bidirectional problems, float32 arithmetic) requires
+ * d <= 32, m <= 128 and L <= 1024 -- with L <= 512, d a multiple of 8 and m
+ * a multiple of 16 it is one launch whose matrix products take float32
+ * operands as two bf16 parts each (relative error near 2^-17 per product,
+ * float32 accumulation), otherwise two launches on the vector ALUs; the
+ * choice depends on (L, d, m) only, never on B or H; GENERIC handles f32
  * and bf16 with d <= 64.  AUTO tries them in that order.  The backward pass
  * has MFMA and GENERIC families (SMALL returns FAVOR_ERR_UNSUPPORTED). */
 typedef enum {

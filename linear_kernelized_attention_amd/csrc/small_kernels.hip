@@ -324,6 +324,378 @@ __global__ __launch_bounds__(NT) void readout_kernel(Args a) {
   }
 }
 
+dim3 head_grid(int x, long long BH);
+
+// ---------------------------------------------------------------------------
+// One launch for the smallest problems (L <= 512, d a multiple of 8 up to 32,
+// m a multiple of 16 up to 128): a block per (head, 32 queries) forms the
+// head's whole key state itself -- every block of a head repeats that work,
+// which at these sizes costs less than a second launch and a round trip of
+// partial states through memory -- and then reads out its own queries.
+//
+// The products run on the matrix cores (v_mfma_f32_16x16x32_bf16; lane
+// l = 16 g + c holds A[c][8 g + j], B[8 g + j][c] and C[4 g + r][c]) with
+// float32 operands split into two bf16 parts, x = hi + lo with
+// |x - hi - lo| <= 2^-18 |x|, and a.b taken as hi.hi + hi.lo + lo.hi with
+// float32 accumulation: a relative error near 2^-17 per product, well
+// inside the float32 parity bar, at three matrix products per product.
+//
+// Wave (row tile rt, half h) of the 2 m / 16 waves owns Omega rows
+// 16 rt .. 16 rt + 15 (features: their sines and cosines, or the one map)
+// and half h of the key steps of 32 tokens:
+//   keys:  P = K Omega~^T per 16-token tile (lane: token 4 g + r, row c),
+//          the features times the key weight, and the projection's C
+//          fragments of the step's two tiles taken as the A fragment of
+//          S_f += phi_f^T [v, 1] (token slot 4 tile + r of group g), the
+//          value rows staged transposed in LDS in that slot order;
+//   the two halves' states are added through LDS;
+//   queries: P^T = Omega~ Q^T (lane: row 4 g + r, query c), the features
+//          as the B fragment and the state's C fragments as the A fragment
+//          of num^T = S^T phi(q)^T (slots 0..3 the first feature tile, 4..7
+//          the second), half h taking query tile h of the block;
+//   the row tiles' partial num^T are summed through LDS in tile order and
+//   out = num / den is stored.
+constexpr int FQ = 32;    // queries per block
+constexpr int FLM = 512;  // longest sequence
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+struct Split {
+  bf16x8 hi, lo;
+};
+
+__device__ inline Split split8(const float (&x)[8]) {
+  Split p;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    p.hi[j] = h;
+    p.lo[j] = (__bf16)(x[j] - (float)h);
+  }
+  return p;
+}
+
+__device__ inline floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// c + a b with both operands split: the two small terms first
+__device__ inline floatx4 mma3(const Split& a, const Split& b, floatx4 c) {
+  c = mma(a.lo, b.hi, c);
+  c = mma(a.hi, b.lo, c);
+  return mma(a.hi, b.hi, c);
+}
+
+// Elements 8 g .. 8 g + 7 of a row (zero from column d on; d is a multiple
+// of 8, so a group is either whole or past the row): the operand piece of
+// lane group g.  The load always reads inside the row.
+__device__ inline void load_piece(const float* row, int g, int d, float (&x)[8]) {
+  const bool ok = 8 * g < d;
+  const float4* p = (const float4*)(row + (ok ? 8 * g : 0));
+  const float4 a = p[0], b = p[1];
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = ok ? v[j] : 0.f;
+}
+__device__ inline void load_piece(const uint16_t* row, int g, int d, float (&x)[8]) {
+  const bool ok = 8 * g < d;
+  const uint4 u = *(const uint4*)(row + (ok ? 8 * g : 0));
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = ok ? __uint_as_float(w[j] << 16) : 0.f;
+    x[2 * j + 1] = ok ? __uint_as_float(w[j] & 0xffff0000u) : 0.f;
+  }
+}
+
+// Slot of token t (0..31) of a key step in the contraction's K order: the
+// projection tile t / 16 puts token 16 (t / 16) + 4 g + r in group g,
+// register r, which the A fragment takes as slot 8 g + 4 (t / 16) + r.
+__device__ inline int token_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
+
+// LDS of the one-launch kernel: per-token key weights and exponent offsets,
+// the queries' offsets, then one region that first holds the transposed
+// value rows (hi and lo parts) and later the halves' states and the row
+// tiles' partial outputs.
+struct FusedLds {
+  size_t vrow;      // elements per transposed value row
+  size_t region;    // bytes of the shared region
+  size_t total;     // bytes
+};
+__host__ __device__ inline FusedLds fused_lds(int L, int d, int m, int kind) {
+  const int nct = (d + 1 + 15) / 16, ncp = 16 * nct;
+  const int lp = (L + 31) / 32 * 32;
+  const int nrt = m / 16, nw = 2 * nrt, ft = kind == KIND_TRIG ? 2 : 1;
+  FusedLds f;
+  f.vrow = (size_t)lp + 8;
+  const size_t vst = 2 * (size_t)ncp * f.vrow * sizeof(uint16_t);
+  const size_t xch = (size_t)nw * ft * nct * 64 * 4 * sizeof(float);
+  const size_t red = (size_t)nrt * FQ * ncp * sizeof(float);
+  f.region = vst > xch + red ? vst : xch + red;
+  f.total = (2 * FLM + FQ) * sizeof(float) + f.region;
+  return f;
+}
+
+template <typename T, int KIND, int NCT>
+__global__ __launch_bounds__(1024) void fused_kernel(Args a) {
+  constexpr bool TRIG = KIND == KIND_TRIG;
+  constexpr bool POS = KIND == KIND_POS;
+  constexpr int FT = TRIG ? 2 : 1;
+  constexpr int NCP = 16 * NCT;
+  const int qb = blockIdx.x;
+  const long long bh = blockIdx.y + (long long)gridDim.y * blockIdx.z;
+  if (bh >= a.BH) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int d = a.d, m = a.m, L = a.L;
+  const int nrt = m / 16, NT = 2 * nrt * 64;
+  const int rt = wv % nrt, half = wv / nrt;
+  const int LP = (L + 31) / 32 * 32;
+  const size_t head = (size_t)bh * L * d;
+  const T* K = (const T*)a.k + head;
+  const T* V = (const T*)a.v + head;
+  const T* Q = (const T*)a.q + head;
+  const FusedLds lay = fused_lds(L, d, m, KIND);
+  const int VR = (int)lay.vrow;
+  const float rsd = rsqrtf((float)d);   // |x~|^2 = |x|^2 / sqrt(d)
+
+  extern __shared__ __attribute__((aligned(16))) float fsm[];
+  float* cw = fsm;                  // key weight per token (0 past L)
+  float* ho = fsm + FLM;            // positive map: exponent offset per token
+  float* hqs = fsm + 2 * FLM;       // query exponent offsets of the block
+  unsigned char* region = (unsigned char*)(fsm + 2 * FLM + FQ);
+  uint16_t* vst = (uint16_t*)region;   // [2][NCP][VR]: hi, lo parts
+
+  // Register operands first, so that their loads overlap the staging's:
+  // Omega~ rows 16 rt + c, columns 8 g.. (scaled for the device map) -- the
+  // B fragment of the key projection and the A fragment of the query one;
+  // this wave's query piece; the pieces of its first key step.
+  const int nks = LP / 32, ksh = (nks + 1) / 2;
+  const int ks0 = half ? ksh : 0, ks1 = half ? nks : ksh;
+  float xo[8], xq[8], xk[2][8];
+  load_piece(a.omega + (size_t)(16 * rt + c) * d, g, d, xo);
+  const int qi = qb * FQ + 16 * half + c;
+  load_piece(Q + (size_t)min(qi, L - 1) * d, g, d, xq);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) load_piece(K + (size_t)min(32 * ks0 + 16 * tt + c, L - 1) * d, g, d, xk[tt]);
+
+  // --- staging, in rounds whose loads are all issued before any is used
+  // (indices clamped into the arrays, no load in a branch): per round a
+  // thread takes one token's key norm (key weight, exponent offset) and two
+  // value tasks, a task being a token pair (tokens 2 p, 2 p + 1, which sit
+  // in adjacent slots) x 8 columns of the rows [v, 1, 0..], stored
+  // transposed as hi and lo parts.
+  const int NCG = NCP / 8;
+  const int ntask = LP / 2 * NCG;
+  const int nround = max((LP + NT - 1) / NT, (ntask + 2 * NT - 1) / (2 * NT));
+  for (int rd = 0; rd < nround; ++rd) {
+    const int t = rd * NT + tid;
+    float kr[4][8];
+#pragma unroll
+    for (int g8 = 0; g8 < 4; ++g8) load_piece(K + (size_t)min(t, L - 1) * d, g8, d, kr[g8]);
+    float x[2][2][8];
+    int task[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      task[j] = (2 * rd + j) * NT + tid;
+      const int tk = min(task[j], ntask - 1);
+      const int p = tk / NCG, cg = tk % NCG;
+      const int cgl = min(cg, d / 8 - 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        load_piece(V + (size_t)min(2 * p + u, L - 1) * d + 8 * cgl, 0, 8, x[j][u]);
+    }
+    if (t < LP) {
+      float ss = 0.f;
+#pragma unroll
+      for (int g8 = 0; g8 < 4; ++g8)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) ss = fmaf(kr[g8][jj], kr[g8][jj], ss);
+      const float h = 0.5f * LOG2E * ss * rsd;
+      cw[t] = t < L ? (TRIG ? __builtin_amdgcn_exp2f(h) : 1.f) : 0.f;
+      ho[t] = POS ? h : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (task[j] >= ntask) continue;
+      const int p = task[j] / NCG, cg = task[j] % NCG;
+      const int t0 = 2 * p;
+      const int slot = (t0 & ~31) + token_slot(t0 & 31);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int col = 8 * cg + jj;
+        float v0 = col < d ? x[j][0][jj] : col == d ? 1.f : 0.f;
+        float v1 = col < d ? x[j][1][jj] : col == d ? 1.f : 0.f;
+        if (t0 >= L) v0 = 0.f;
+        if (t0 + 1 >= L) v1 = 0.f;
+        const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+        const __bf16 l0 = (__bf16)(v0 - (float)h0), l1 = (__bf16)(v1 - (float)h1);
+        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+        const bf16x2 hv = {h0, h1}, lv = {l0, l1};
+        *(bf16x2*)(vst + (size_t)col * VR + slot) = hv;
+        *(bf16x2*)(vst + ((size_t)NCP + col) * VR + slot) = lv;
+      }
+    }
+  }
+  Split om;
+  {
+    const float sc = (TRIG ? INV_2PI : POS ? LOG2E : 1.f) * rsqrtf(sqrtf((float)d));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xo[j] *= sc;
+    om = split8(xo);
+  }
+  __syncthreads();
+
+  // --- key state of this wave's rows over its half of the key steps; the
+  // next step's key pieces are loaded while this one is computed
+  floatx4 acc[FT][NCT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) acc[f][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = ks0; ks < ks1; ++ks) {
+    float xn[2][8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) load_piece(K + (size_t)min(32 * ks + 32 + 16 * tt + c, L - 1) * d, g, d, xn[tt]);
+    float fa[FT][8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const floatx4 P = mma3(split8(xk[tt]), om, floatx4{0.f, 0.f, 0.f, 0.f});
+      const int t4 = 32 * ks + 16 * tt + 4 * g;
+      const float4 w4 = *(const float4*)(cw + t4);
+      const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+      float hh[4] = {0.f, 0.f, 0.f, 0.f};
+      if (POS) {
+        const float4 h4 = *(const float4*)(ho + t4);
+        hh[0] = h4.x; hh[1] = h4.y; hh[2] = h4.z; hh[3] = h4.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (TRIG) {
+          fa[0][4 * tt + r] = __builtin_amdgcn_sinf(P[r]) * w[r];
+          fa[FT - 1][4 * tt + r] = __builtin_amdgcn_cosf(P[r]) * w[r];
+        } else if (POS) {
+          fa[0][4 * tt + r] = __builtin_amdgcn_exp2f(P[r] - hh[r]) * w[r];
+        } else {
+          fa[0][4 * tt + r] = fmaxf(P[r], 0.f) * w[r];
+        }
+      }
+    }
+    Split A[FT];
+#pragma unroll
+    for (int f = 0; f < FT; ++f) A[f] = split8(fa[f]);
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) {
+      Split Bv;
+      Bv.hi = *(const bf16x8*)(vst + (size_t)(16 * n + c) * VR + 32 * ks + 8 * g);
+      Bv.lo = *(const bf16x8*)(vst + (size_t)(NCP + 16 * n + c) * VR + 32 * ks + 8 * g);
+#pragma unroll
+      for (int f = 0; f < FT; ++f) acc[f][n] = mma3(A[f], Bv, acc[f][n]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xk[tt][j] = xn[tt][j];
+  }
+
+  // --- the two halves' states, added in the same order by both waves
+  __syncthreads();
+  floatx4* xch = (floatx4*)region;   // [nw][FT][NCT][64]
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) xch[((size_t)(wv * FT + f) * NCT + n) * 64 + lane] = acc[f][n];
+  __syncthreads();
+  const int pw = (1 - half) * nrt + rt;
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) {
+      const floatx4 o = xch[((size_t)(pw * FT + f) * NCT + n) * 64 + lane];
+      acc[f][n] = half ? o + acc[f][n] : acc[f][n] + o;
+    }
+
+  // --- readout of query tile `half` of the block, this wave's rows
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = fmaf(xq[j], xq[j], ss);
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float hq = 0.5f * LOG2E * ss * rsd;
+  const floatx4 Pq = mma3(om, split8(xq), floatx4{0.f, 0.f, 0.f, 0.f});
+  float fb[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (TRIG) {
+      fb[r] = __builtin_amdgcn_sinf(Pq[r]);
+      fb[4 + r] = __builtin_amdgcn_cosf(Pq[r]);
+    } else {
+      fb[r] = POS ? __builtin_amdgcn_exp2f(Pq[r] - hq) : fmaxf(Pq[r], 0.f);
+      fb[4 + r] = 0.f;
+    }
+  }
+  const Split Bq = split8(fb);
+  float* red = (float*)(region + (size_t)nrt * 2 * FT * NCT * 64 * 4 * sizeof(float));  // [nrt][FQ][NCP]
+#pragma unroll
+  for (int n = 0; n < NCT; ++n) {
+    float sa[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sa[r] = acc[0][n][r];
+      sa[4 + r] = FT == 2 ? acc[FT - 1][n][r] : 0.f;
+    }
+    const floatx4 o = mma3(split8(sa), Bq, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((size_t)rt * FQ + 16 * half + c) * NCP + 16 * n + 4 * g + r] = o[r];
+  }
+  if (rt == 0 && g == 0) hqs[16 * half + c] = hq;
+  __syncthreads();
+
+  // --- out = num / den, the row tiles summed in order
+  T* O = (T*)a.out + head;
+  for (int i = tid; i < FQ * d; i += NT) {
+    const int q = i / d, col = i % d;
+    const int qg = qb * FQ + q;
+    if (qg >= L) continue;
+    float num = 0.f, den = 0.f;
+    for (int r2 = 0; r2 < nrt; ++r2) {
+      num += red[((size_t)r2 * FQ + q) * NCP + col];
+      den += red[((size_t)r2 * FQ + q) * NCP + d];
+    }
+    st(O, (size_t)qg * d + col, num / den);
+    // row normalisers in the pages' units: the device denominator times
+    // m^-1 and, for trig, the query weight exp(|q~|^2 / 2)
+    if (a.den && col == 0) {
+      float scale = 1.0f / (float)m;
+      if (TRIG) scale *= __builtin_amdgcn_exp2f(hqs[q]);
+      a.den[(size_t)bh * L + qg] = den * scale;
+    }
+  }
+}
+
+// The choice depends on the head's shape only, never on the number of
+// heads, so that a head's output does not change with the batch around it.
+bool fused_supports(const Problem& p) {
+  return !p.causal && p.L >= 1 && p.L <= FLM && p.d % 8 == 0 && p.d >= 8 && p.d <= DM &&
+         p.m % 16 == 0 && p.m >= 16 && p.m <= MM;
+}
+
+template <typename T, int KIND>
+hipError_t launch_fused_kind(const Problem& p, const Args& a, hipStream_t s) {
+  const FusedLds lay = fused_lds(p.L, p.d, p.m, KIND);
+  const int nct = (p.d + 1 + 15) / 16;
+  auto kern = nct == 1 ? fused_kernel<T, KIND, 1> : nct == 2 ? fused_kernel<T, KIND, 2> : fused_kernel<T, KIND, 3>;
+  static bool raised[3] = {false, false, false};
+  if (!raised[nct - 1]) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    raised[nct - 1] = true;
+  }
+  const int nqb = (p.L + FQ - 1) / FQ;
+  hipLaunchKernelGGL(kern, head_grid(nqb, p.BH), dim3(8 * p.m), lay.total, s, a);
+  return hipSuccess;
+}
+
 dim3 head_grid(int x, long long BH) {
   // blockIdx.y + gridDim.y * blockIdx.z enumerates the heads
   const long long y = BH < 65535 ? BH : 65535;
@@ -341,6 +713,16 @@ hipError_t run_typed(const Problem& p, const Buffers& b, hipStream_t s, PhaseHoo
   a.nkb = (p.L + TB - 1) / TB;
   const int nqb = (p.L + TQ - 1) / TQ;
   const int reps = phase_reps(hook);
+  if (fused_supports(p)) {
+    phase_begin(hook, s, "small_fused");
+    for (int r = 0; r < reps; ++r) {
+      if (p.kind == KIND_TRIG) (void)launch_fused_kind<T, KIND_TRIG>(p, a, s);
+      else if (p.kind == KIND_POS) (void)launch_fused_kind<T, KIND_POS>(p, a, s);
+      else (void)launch_fused_kind<T, KIND_RELU>(p, a, s);
+    }
+    phase_end(hook, s, reps);
+    return hipGetLastError();
+  }
   // feature loops over 16 or 32 columns
   auto kst = p.d <= 16 ? state_kernel<T, 16> : state_kernel<T, DM>;
   auto kro = p.d <= 16 ? readout_kernel<T, 16> : readout_kernel<T, DM>;

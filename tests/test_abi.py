@@ -117,8 +117,9 @@ def test_workspace_sizes_monotone():
 
 
 def test_resolve_path():
-    # the small float32 workload runs on the two-launch small path; the
-    # generic kernels take it when asked, MFMA cannot
+    # the small float32 workload runs on the small path (its one-launch
+    # kernel at this size); the generic kernels take it when asked, MFMA
+    # cannot
     R = F.favor_attention_resolve_path
     assert R(1, 1, 512, 16, 64, "f32", "trig", False) == "small"
     assert R(1, 1, 512, 16, 64, "f32", "trig", False, "generic") == "generic"

@@ -59,6 +59,17 @@ SMALL = [
     # m = 512: the bidirectional MFMA readout in two feature passes (the
     # causal and float32 cases run on the generic kernels)
     (1, 2, 300, 64, 512, "bf16"),
+    # the small path's one-launch kernel at its limits: d = 32 (three value
+    # column tiles), m = 128 (16 waves), L = 512 (16 key steps per half);
+    # d = 8 (one column tile) with m = 16 (two waves) and a ragged tail;
+    # d = 24 with three Omega row tiles
+    (1, 1, 512, 32, 128, "f32"),
+    (1, 2, 33, 8, 16, "f32"),
+    (2, 1, 200, 24, 48, "bf16"),
+    # the small path's two launches: past the one-launch kernel's sequence
+    # limit, and d and m that are not multiples of 8 and 16
+    (1, 1, 700, 16, 64, "f32"),
+    (1, 2, 300, 20, 40, "f32"),
 ]
 
 
