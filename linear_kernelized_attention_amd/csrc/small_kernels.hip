@@ -340,38 +340,68 @@ dim3 head_grid(int x, long long BH);
 // float32 accumulation: a relative error near 2^-17 per product, well
 // inside the float32 parity bar, at three matrix products per product.
 //
-// Wave (row tile rt, half h) of the 2 m / 16 waves owns Omega rows
-// 16 rt .. 16 rt + 15 (features: their sines and cosines, or the one map)
-// and half h of the key steps of 32 tokens:
+// The block's waves form nrt = m / 16 row tiles x FTS token splits;
+// wave (row tile rt, split ts) owns Omega rows 16 rt .. 16 rt + 15
+// (features: their sines and cosines, or the one map) and split ts of the
+// key steps of 32 tokens:
+//   staging: the keys split into hi and lo parts in LDS (A fragment
+//          pieces), the value rows transposed and split in the slot order
+//          below, the key weights and exponent offsets per token;
 //   keys:  P = K Omega~^T per 16-token tile (lane: token 4 g + r, row c),
 //          the features times the key weight, and the projection's C
 //          fragments of the step's two tiles taken as the A fragment of
-//          S_f += phi_f^T [v, 1] (token slot 4 tile + r of group g), the
-//          value rows staged transposed in LDS in that slot order;
-//   the two halves' states are added through LDS;
+//          S_f += phi_f^T [v, 1] (token slot 8 g + 4 tile + r); the z
+//          column's B fragment is the constant (1 in column 0);
+//   the splits' states are added through LDS in split order;
 //   queries: P^T = Omega~ Q^T (lane: row 4 g + r, query c), the features
 //          as the B fragment and the state's C fragments as the A fragment
 //          of num^T = S^T phi(q)^T (slots 0..3 the first feature tile, 4..7
-//          the second), half h taking query tile h of the block;
+//          the second), splits 0 and 1 taking query tiles 0 and 1;
 //   the row tiles' partial num^T are summed through LDS in tile order and
 //   out = num / den is stored.
 constexpr int FQ = 32;    // queries per block
+// token splits (waves per Omega row tile): 2 measured faster than 16 / nrt
+// on the float32 workload (10.8 against 12.1 us per launch); the loop is
+// bound by the SIMDs' instruction issue, which more waves do not raise
+constexpr int FTS = 2;
 constexpr int FLM = 512;  // longest sequence
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 struct Split {
   bf16x8 hi, lo;
 };
 
-__device__ inline Split split8(const float (&x)[8]) {
+// Selectors of v_dot2_f32_bf16 that subtract the low or the high bf16 half
+// of a packed word from a float32 addend: (-1, 0) and (0, -1).  Made in
+// registers (an inline constant would not be read as a bf16 pair).
+struct NegSel {
+  uint32_t lo, hi;
+};
+__device__ inline NegSel neg_selectors() {
+  NegSel s{0x0000BF80u, 0xBF800000u};
+  asm("" : "+v"(s.lo), "+v"(s.hi));
+  return s;
+}
+
+// x = hi + lo: hi = bf16(x) (round to nearest even), lo = bf16(x - hi)
+// where x - hi is exact in float32 and comes from one v_dot2_f32_bf16 of
+// the packed hi pair with a selector (x - 1 * hi_0 - 0 * hi_1).
+__device__ inline Split split8(const float (&x)[8], NegSel ns) {
   Split p;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    p.hi[j] = h;
-    p.lo[j] = (__bf16)(x[j] - (float)h);
+  for (int j = 0; j < 8; j += 2) {
+    bf16x2 h;
+    h[0] = (__bf16)x[j];
+    h[1] = (__bf16)x[j + 1];
+    const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, ns.lo), x[j], false);
+    const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, ns.hi), x[j + 1], false);
+    p.hi[j] = h[0];
+    p.hi[j + 1] = h[1];
+    p.lo[j] = (__bf16)l0;
+    p.lo[j + 1] = (__bf16)l1;
   }
   return p;
 }
@@ -416,41 +446,46 @@ __device__ inline int token_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >>
 
 // LDS of the one-launch kernel: per-token key weights and exponent offsets,
 // the queries' offsets, then one region that first holds the transposed
-// value rows (hi and lo parts) and later the halves' states and the row
+// value rows and the split keys, later the halves' states and the row
 // tiles' partial outputs.
 struct FusedLds {
   size_t vrow;      // elements per transposed value row
+  size_t kst;       // byte offset of the split keys in the region
   size_t region;    // bytes of the shared region
   size_t total;     // bytes
 };
 __host__ __device__ inline FusedLds fused_lds(int L, int d, int m, int kind) {
-  const int nct = (d + 1 + 15) / 16, ncp = 16 * nct;
+  const int ncv = (d + 15) / 16 * 16;      // value columns in LDS
+  const int nct = ncv / 16 + 1;            // column tiles with the z tile
   const int lp = (L + 31) / 32 * 32;
-  const int nrt = m / 16, nw = 2 * nrt, ft = kind == KIND_TRIG ? 2 : 1;
+  const int nrt = m / 16, nw = nrt * FTS, ft = kind == KIND_TRIG ? 2 : 1;
   FusedLds f;
   f.vrow = (size_t)lp + 8;
-  const size_t vst = 2 * (size_t)ncp * f.vrow * sizeof(uint16_t);
+  f.kst = 2 * (size_t)ncv * f.vrow * sizeof(uint16_t);
+  const size_t kst = 2 * (size_t)4 * lp * 8 * sizeof(uint16_t);
   const size_t xch = (size_t)nw * ft * nct * 64 * 4 * sizeof(float);
-  const size_t red = (size_t)nrt * FQ * ncp * sizeof(float);
-  f.region = vst > xch + red ? vst : xch + red;
+  const size_t red = (size_t)nrt * FQ * 16 * nct * sizeof(float);
+  f.region = f.kst + kst > xch + red ? f.kst + kst : xch + red;
   f.total = (2 * FLM + FQ) * sizeof(float) + f.region;
   return f;
 }
 
-template <typename T, int KIND, int NCT>
+template <typename T, int KIND, int NCTV>
 __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
   constexpr bool TRIG = KIND == KIND_TRIG;
   constexpr bool POS = KIND == KIND_POS;
   constexpr int FT = TRIG ? 2 : 1;
-  constexpr int NCP = 16 * NCT;
+  constexpr int NCT = NCTV + 1;     // value column tiles and the z tile
+  constexpr int NCV = 16 * NCTV;    // value columns staged in LDS
+  constexpr int NCP = 16 * NCT;     // columns of a partial output row
   const int qb = blockIdx.x;
   const long long bh = blockIdx.y + (long long)gridDim.y * blockIdx.z;
   if (bh >= a.BH) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int d = a.d, m = a.m, L = a.L;
-  const int nrt = m / 16, NT = 2 * nrt * 64;
-  const int rt = wv % nrt, half = wv / nrt;
+  const int nrt = m / 16, TS = FTS, NT = nrt * TS * 64;
+  const int rt = wv % nrt, ts = wv / nrt;
   const int LP = (L + 31) / 32 * 32;
   const size_t head = (size_t)bh * L * d;
   const T* K = (const T*)a.k + head;
@@ -459,34 +494,32 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
   const FusedLds lay = fused_lds(L, d, m, KIND);
   const int VR = (int)lay.vrow;
   const float rsd = rsqrtf((float)d);   // |x~|^2 = |x|^2 / sqrt(d)
+  const NegSel ns = neg_selectors();
 
   extern __shared__ __attribute__((aligned(16))) float fsm[];
   float* cw = fsm;                  // key weight per token (0 past L)
   float* ho = fsm + FLM;            // positive map: exponent offset per token
   float* hqs = fsm + 2 * FLM;       // query exponent offsets of the block
   unsigned char* region = (unsigned char*)(fsm + 2 * FLM + FQ);
-  uint16_t* vst = (uint16_t*)region;   // [2][NCP][VR]: hi, lo parts
+  uint16_t* vst = (uint16_t*)region;                 // [2][NCV][VR]: hi, lo
+  bf16x8* kst = (bf16x8*)(region + lay.kst);         // [2][4][LP]: hi, lo (zero past d)
 
   // Register operands first, so that their loads overlap the staging's:
   // Omega~ rows 16 rt + c, columns 8 g.. (scaled for the device map) -- the
-  // B fragment of the key projection and the A fragment of the query one;
-  // this wave's query piece; the pieces of its first key step.
-  const int nks = LP / 32, ksh = (nks + 1) / 2;
-  const int ks0 = half ? ksh : 0, ks1 = half ? nks : ksh;
-  float xo[8], xq[8], xk[2][8];
+  // B fragment of the key projection and the A fragment of the query one --
+  // and this wave's query piece.
+  float xo[8], xq[8];
   load_piece(a.omega + (size_t)(16 * rt + c) * d, g, d, xo);
-  const int qi = qb * FQ + 16 * half + c;
+  const int qi = qb * FQ + 16 * (ts & 1) + c;
   load_piece(Q + (size_t)min(qi, L - 1) * d, g, d, xq);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) load_piece(K + (size_t)min(32 * ks0 + 16 * tt + c, L - 1) * d, g, d, xk[tt]);
 
   // --- staging, in rounds whose loads are all issued before any is used
   // (indices clamped into the arrays, no load in a branch): per round a
-  // thread takes one token's key norm (key weight, exponent offset) and two
-  // value tasks, a task being a token pair (tokens 2 p, 2 p + 1, which sit
-  // in adjacent slots) x 8 columns of the rows [v, 1, 0..], stored
-  // transposed as hi and lo parts.
-  const int NCG = NCP / 8;
+  // thread takes one token (its key row split into LDS, its key weight and
+  // exponent offset) and two value tasks, a task being a token pair
+  // (tokens 2 p, 2 p + 1, which sit in adjacent slots) x 8 value columns,
+  // stored transposed as hi and lo parts.
+  const int NCG = NCV / 8;
   const int ntask = LP / 2 * NCG;
   const int nround = max((LP + NT - 1) / NT, (ntask + 2 * NT - 1) / (2 * NT));
   for (int rd = 0; rd < nround; ++rd) {
@@ -500,18 +533,21 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
     for (int j = 0; j < 2; ++j) {
       task[j] = (2 * rd + j) * NT + tid;
       const int tk = min(task[j], ntask - 1);
-      const int p = tk / NCG, cg = tk % NCG;
-      const int cgl = min(cg, d / 8 - 1);
+      const int p = tk / NCG, cg = min(tk % NCG, d / 8 - 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        load_piece(V + (size_t)min(2 * p + u, L - 1) * d + 8 * cgl, 0, 8, x[j][u]);
+        load_piece(V + (size_t)min(2 * p + u, L - 1) * d + 8 * cg, 0, 8, x[j][u]);
     }
     if (t < LP) {
       float ss = 0.f;
 #pragma unroll
-      for (int g8 = 0; g8 < 4; ++g8)
+      for (int g8 = 0; g8 < 4; ++g8) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) ss = fmaf(kr[g8][jj], kr[g8][jj], ss);
+        const Split ks = split8(kr[g8], ns);
+        kst[(size_t)g8 * LP + t] = ks.hi;
+        kst[(size_t)(4 + g8) * LP + t] = ks.lo;
+      }
       const float h = 0.5f * LOG2E * ss * rsd;
       cw[t] = t < L ? (TRIG ? __builtin_amdgcn_exp2f(h) : 1.f) : 0.f;
       ho[t] = POS ? h : 0.f;
@@ -525,16 +561,18 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int col = 8 * cg + jj;
-        float v0 = col < d ? x[j][0][jj] : col == d ? 1.f : 0.f;
-        float v1 = col < d ? x[j][1][jj] : col == d ? 1.f : 0.f;
+        float v0 = col < d ? x[j][0][jj] : 0.f;
+        float v1 = col < d ? x[j][1][jj] : 0.f;
         if (t0 >= L) v0 = 0.f;
         if (t0 + 1 >= L) v1 = 0.f;
-        const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
-        const __bf16 l0 = (__bf16)(v0 - (float)h0), l1 = (__bf16)(v1 - (float)h1);
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        const bf16x2 hv = {h0, h1}, lv = {l0, l1};
+        bf16x2 hv;
+        hv[0] = (__bf16)v0;
+        hv[1] = (__bf16)v1;
+        bf16x2 lv;
+        lv[0] = (__bf16)__builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, ns.lo), v0, false);
+        lv[1] = (__bf16)__builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, ns.hi), v1, false);
         *(bf16x2*)(vst + (size_t)col * VR + slot) = hv;
-        *(bf16x2*)(vst + ((size_t)NCP + col) * VR + slot) = lv;
+        *(bf16x2*)(vst + ((size_t)NCV + col) * VR + slot) = lv;
       }
     }
   }
@@ -543,25 +581,31 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
     const float sc = (TRIG ? INV_2PI : POS ? LOG2E : 1.f) * rsqrtf(sqrtf((float)d));
 #pragma unroll
     for (int j = 0; j < 8; ++j) xo[j] *= sc;
-    om = split8(xo);
+    om = split8(xo, ns);
   }
+  // the z column's B fragment: 1 in column 0 for every token slot
+  bf16x8 bz;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bz[j] = (__bf16)(c == 0 ? 1.f : 0.f);
   __syncthreads();
 
-  // --- key state of this wave's rows over its half of the key steps; the
-  // next step's key pieces are loaded while this one is computed
+  // --- key state of this wave's rows over its split of the key steps
   floatx4 acc[FT][NCT];
 #pragma unroll
   for (int f = 0; f < FT; ++f)
 #pragma unroll
     for (int n = 0; n < NCT; ++n) acc[f][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int nks = LP / 32;
+  const int ks0 = ts * nks / TS, ks1 = (ts + 1) * nks / TS;
   for (int ks = ks0; ks < ks1; ++ks) {
-    float xn[2][8];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) load_piece(K + (size_t)min(32 * ks + 32 + 16 * tt + c, L - 1) * d, g, d, xn[tt]);
     float fa[FT][8];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const floatx4 P = mma3(split8(xk[tt]), om, floatx4{0.f, 0.f, 0.f, 0.f});
+      const int t = 32 * ks + 16 * tt + c;
+      Split kp;
+      kp.hi = kst[(size_t)g * LP + t];
+      kp.lo = kst[(size_t)(4 + g) * LP + t];
+      const floatx4 P = mma3(kp, om, floatx4{0.f, 0.f, 0.f, 0.f});
       const int t4 = 32 * ks + 16 * tt + 4 * g;
       const float4 w4 = *(const float4*)(cw + t4);
       const float w[4] = {w4.x, w4.y, w4.z, w4.w};
@@ -584,22 +628,22 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
     }
     Split A[FT];
 #pragma unroll
-    for (int f = 0; f < FT; ++f) A[f] = split8(fa[f]);
+    for (int f = 0; f < FT; ++f) A[f] = split8(fa[f], ns);
 #pragma unroll
-    for (int n = 0; n < NCT; ++n) {
+    for (int n = 0; n < NCTV; ++n) {
       Split Bv;
       Bv.hi = *(const bf16x8*)(vst + (size_t)(16 * n + c) * VR + 32 * ks + 8 * g);
-      Bv.lo = *(const bf16x8*)(vst + (size_t)(NCP + 16 * n + c) * VR + 32 * ks + 8 * g);
+      Bv.lo = *(const bf16x8*)(vst + (size_t)(NCV + 16 * n + c) * VR + 32 * ks + 8 * g);
 #pragma unroll
       for (int f = 0; f < FT; ++f) acc[f][n] = mma3(A[f], Bv, acc[f][n]);
     }
+    // z: the B fragment is exact in bf16, so two products
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xk[tt][j] = xn[tt][j];
+    for (int f = 0; f < FT; ++f) acc[f][NCTV] = mma(A[f].hi, bz, mma(A[f].lo, bz, acc[f][NCTV]));
   }
 
-  // --- the two halves' states, added in the same order by both waves
+  // --- the splits' states, added in split order by the two waves of each
+  // row tile that read out (splits 0 and 1: the same sum, bit for bit)
   __syncthreads();
   floatx4* xch = (floatx4*)region;   // [nw][FT][NCT][64]
 #pragma unroll
@@ -607,52 +651,57 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
 #pragma unroll
     for (int n = 0; n < NCT; ++n) xch[((size_t)(wv * FT + f) * NCT + n) * 64 + lane] = acc[f][n];
   __syncthreads();
-  const int pw = (1 - half) * nrt + rt;
+  const bool reader = ts < 2;
+  if (reader) {
 #pragma unroll
-  for (int f = 0; f < FT; ++f)
+    for (int f = 0; f < FT; ++f)
 #pragma unroll
-    for (int n = 0; n < NCT; ++n) {
-      const floatx4 o = xch[((size_t)(pw * FT + f) * NCT + n) * 64 + lane];
-      acc[f][n] = half ? o + acc[f][n] : acc[f][n] + o;
-    }
-
-  // --- readout of query tile `half` of the block, this wave's rows
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ss = fmaf(xq[j], xq[j], ss);
-  ss += __shfl_xor(ss, 16);
-  ss += __shfl_xor(ss, 32);
-  const float hq = 0.5f * LOG2E * ss * rsd;
-  const floatx4 Pq = mma3(om, split8(xq), floatx4{0.f, 0.f, 0.f, 0.f});
-  float fb[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (TRIG) {
-      fb[r] = __builtin_amdgcn_sinf(Pq[r]);
-      fb[4 + r] = __builtin_amdgcn_cosf(Pq[r]);
-    } else {
-      fb[r] = POS ? __builtin_amdgcn_exp2f(Pq[r] - hq) : fmaxf(Pq[r], 0.f);
-      fb[4 + r] = 0.f;
-    }
+      for (int n = 0; n < NCT; ++n) {
+        floatx4 sum = xch[((size_t)(rt * FT + f) * NCT + n) * 64 + lane];
+        for (int s2 = 1; s2 < TS; ++s2) sum += xch[((size_t)((s2 * nrt + rt) * FT + f) * NCT + n) * 64 + lane];
+        acc[f][n] = sum;
+      }
   }
-  const Split Bq = split8(fb);
-  float* red = (float*)(region + (size_t)nrt * 2 * FT * NCT * 64 * 4 * sizeof(float));  // [nrt][FQ][NCP]
+
+  // --- readout of query tile ts (splits 0 and 1) of the block, this wave's rows
+  float* red = (float*)(region + (size_t)nrt * TS * FT * NCT * 64 * 4 * sizeof(float));  // [nrt][FQ][NCP]
+  if (reader) {
+    float ss = 0.f;
 #pragma unroll
-  for (int n = 0; n < NCT; ++n) {
-    float sa[8];
+    for (int j = 0; j < 8; ++j) ss = fmaf(xq[j], xq[j], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float hq = 0.5f * LOG2E * ss * rsd;
+    const floatx4 Pq = mma3(om, split8(xq, ns), floatx4{0.f, 0.f, 0.f, 0.f});
+    float fb[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sa[r] = acc[0][n][r];
-      sa[4 + r] = FT == 2 ? acc[FT - 1][n][r] : 0.f;
+      if (TRIG) {
+        fb[r] = __builtin_amdgcn_sinf(Pq[r]);
+        fb[4 + r] = __builtin_amdgcn_cosf(Pq[r]);
+      } else {
+        fb[r] = POS ? __builtin_amdgcn_exp2f(Pq[r] - hq) : fmaxf(Pq[r], 0.f);
+        fb[4 + r] = 0.f;
+      }
     }
-    const floatx4 o = mma3(split8(sa), Bq, floatx4{0.f, 0.f, 0.f, 0.f});
+    const Split Bq = split8(fb, ns);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[((size_t)rt * FQ + 16 * half + c) * NCP + 16 * n + 4 * g + r] = o[r];
+    for (int n = 0; n < NCT; ++n) {
+      float sa[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sa[r] = acc[0][n][r];
+        sa[4 + r] = FT == 2 ? acc[FT - 1][n][r] : 0.f;
+      }
+      const floatx4 o = mma3(split8(sa, ns), Bq, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((size_t)rt * FQ + 16 * ts + c) * NCP + 16 * n + 4 * g + r] = o[r];
+    }
+    if (rt == 0 && g == 0) hqs[16 * ts + c] = hq;
   }
-  if (rt == 0 && g == 0) hqs[16 * half + c] = hq;
   __syncthreads();
 
-  // --- out = num / den, the row tiles summed in order
+  // --- out = num / den, the row tiles summed in order (den: column NCV)
   T* O = (T*)a.out + head;
   for (int i = tid; i < FQ * d; i += NT) {
     const int q = i / d, col = i % d;
@@ -661,7 +710,7 @@ __global__ __launch_bounds__(1024) void fused_kernel(Args a) {
     float num = 0.f, den = 0.f;
     for (int r2 = 0; r2 < nrt; ++r2) {
       num += red[((size_t)r2 * FQ + q) * NCP + col];
-      den += red[((size_t)r2 * FQ + q) * NCP + d];
+      den += red[((size_t)r2 * FQ + q) * NCP + NCV];
     }
     st(O, (size_t)qg * d + col, num / den);
     // row normalisers in the pages' units: the device denominator times
@@ -684,15 +733,16 @@ bool fused_supports(const Problem& p) {
 template <typename T, int KIND>
 hipError_t launch_fused_kind(const Problem& p, const Args& a, hipStream_t s) {
   const FusedLds lay = fused_lds(p.L, p.d, p.m, KIND);
-  const int nct = (p.d + 1 + 15) / 16;
-  auto kern = nct == 1 ? fused_kernel<T, KIND, 1> : nct == 2 ? fused_kernel<T, KIND, 2> : fused_kernel<T, KIND, 3>;
-  static bool raised[3] = {false, false, false};
-  if (!raised[nct - 1]) {
+  const int nctv = (p.d + 15) / 16;
+  auto kern = nctv == 1 ? fused_kernel<T, KIND, 1> : fused_kernel<T, KIND, 2>;
+  static bool raised[2] = {false, false};
+  if (!raised[nctv - 1]) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    raised[nct - 1] = true;
+    raised[nctv - 1] = true;
   }
   const int nqb = (p.L + FQ - 1) / FQ;
-  hipLaunchKernelGGL(kern, head_grid(nqb, p.BH), dim3(8 * p.m), lay.total, s, a);
+  const int nrt = p.m / 16;
+  hipLaunchKernelGGL(kern, head_grid(nqb, p.BH), dim3(64 * nrt * FTS), lay.total, s, a);
   return hipSuccess;
 }
 
