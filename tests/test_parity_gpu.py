@@ -2,9 +2,8 @@
 
 Bar: per-(b, h) relative Frobenius error and the largest per-row relative
 error both <= 1e-4 for float32 inputs and <= 2e-2 for bf16 inputs.  Every
-workload is compared on every output row, except the two L = 32768
-workloads, which are compared on sampled rows that the oracle computes one
-by one."""
+workload is compared on every output row; the two L = 32768 workloads
+are also compared on sampled rows that the oracle computes one by one."""
 import numpy as np
 import pytest
 import torch
@@ -154,6 +153,20 @@ def test_long_sequence_sampled_rows(name):
     for path in _paths(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal):
         got = _run(dev, w.kind, w.causal, path)[..., rows, :]
         assert_parity(got, ref, 2e-2, f"[{path}] {name} sampled rows")
+
+
+@pytest.mark.parametrize("name", ["c4_bidir", "c4_causal"])
+def test_long_sequence_all_rows(name):
+    # L = 32768 at its full shape (B1 H8, key and query norms spread over
+    # [0.5, 2]), every output row against the whole oracle: the bf16 split
+    # partials (bidirectional, many token splits per head, summed by the
+    # split-sum kernel) and the bf16 segment start states (causal, the
+    # longest prefix scans) at the longest sequence
+    w = I.WORKLOADS[name]
+    dev, (q, k, v), W = problem(w.B, w.H, w.L, w.d, w.m, w.dtype, norm_shells=w.norm_shells)
+    ref = O.favor_attention(q, k, v, W, w.kind, w.causal, workers=O.default_workers())
+    for path in _paths(w.B, w.H, w.L, w.d, w.m, w.dtype, w.kind, w.causal):
+        assert_parity(_run(dev, w.kind, w.causal, path), ref, 2e-2, f"[{path}] {name} all rows")
 
 
 @pytest.mark.parametrize("kind", ["trig", "positive"])
