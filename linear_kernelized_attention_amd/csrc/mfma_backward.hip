@@ -21,7 +21,8 @@
 // feature per lane (the transpose of the readout's layout) and the z
 // column; once per call it also writes the (s Omega)^T fragments, whose row
 // order matches the dP C fragments, and (ReLU) the Omega residual
-// fragments.  One block of DPHI_NW waves handles 64 tokens per wave; its
+// fragments.  One block of DPHI_NW waves handles 64 tokens per wave (32 on
+// grids too small to fill the GPU otherwise); its
 // prologue copies these fragments and the Omega~ fragments of the
 // projection into LDS with 16-byte loads.
 // Per Omega row pair and 16-token tile: the projection (4 MFMA), the
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void dphi_prep_kernel(const uint16_t* __restri
     }
 }
 
-template <int KIND, int NPAIR, int NW = DPHI_NW>
+template <int KIND, int NPAIR, int NW = DPHI_NW, int NH32 = 2>
 __global__ __launch_bounds__(NW * 64) void dphi_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ ofrag, DphiPrep prep,
     const uint16_t* __restrict__ Wv, const float* __restrict__ wz,
@@ -166,7 +167,8 @@ __global__ __launch_bounds__(NW * 64) void dphi_kernel(
   const int blk = (int)(lb % nx);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const long long t0 = (long long)blk * NW * QW + (long long)w * QW;
+  constexpr int QWV = 32 * NH32;   // tokens per wave: NH32 halves of 32
+  const long long t0 = (long long)blk * NW * QWV + (long long)w * QWV;
   const size_t head = (size_t)bh * L * D;
 
   // M row fragments and z (prepared per head), the Omega~ fragments, the
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void dphi_kernel(
   constexpr int NH = TRIG ? 2 : 1;   // sin, cos feature halves
   const float sgn = TRIG ? 1.f : POS ? -1.f : 0.f;
 #pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < NH32; ++half) {
     // B operands: x for the projection, w for the contraction with M;
     // tokens past L read the last token
     bf16x8 xf[2][2], wf[2][2];
@@ -330,27 +332,31 @@ __global__ __launch_bounds__(NW * 64) void dphi_kernel(
   }
 }
 
-template <int KIND, int NPAIR, int NW>
+template <int KIND, int NPAIR, int NW, int NH32 = 2>
 hipError_t launch_dphi_nw(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
                           const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
                           bool keys, hipStream_t s) {
   constexpr int M = 32 * NPAIR;
   constexpr int F = KIND == KIND_TRIG ? 2 * M : M;
-  auto kern = dphi_kernel<KIND, NPAIR, NW>;
+  auto kern = dphi_kernel<KIND, NPAIR, NW, NH32>;
   static const bool attr = [&] {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return true;
   }();
   (void)attr;
-  const long long nb = (p.L + NW * QW - 1) / (NW * QW);
+  constexpr int QWV = 32 * NH32;
+  const long long nb = (p.L + NW * QWV - 1) / (NW * QWV);
   const size_t lds = dphi_lds_bytes<M, F, KIND == KIND_RELU>();
   hipLaunchKernelGGL(kern, dim3((unsigned)(nb * p.BH)), dim3(NW * 64), lds, s,
                      X, ofrag, prep, Wv, wz, DX, p.L, p.BH, keys ? 1 : 0);
   return hipGetLastError();
 }
 
-// DPHI_NW waves per block, or half as many when full blocks would leave CUs
-// idle (one block fills a CU's LDS) and halving doubles their number.
+// DPHI_NW waves of 64 tokens per block; when such blocks would leave CUs
+// idle (one block fills a CU's LDS) and half-size blocks would double their
+// number, DPHI_NW waves of 32 tokens instead: the same number of blocks
+// with two waves per SIMD (B8 H8 L1024 trig backward 119.9 -> 106.8 us
+// against four waves of 64 tokens).
 template <int KIND, int NPAIR>
 hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* ofrag,
                          const DphiPrep& prep, const uint16_t* Wv, const float* wz, uint16_t* DX,
@@ -359,7 +365,7 @@ hipError_t launch_dphi_t(const Problem& p, const uint16_t* X, const uint16_t* of
   const long long nb_full = (p.L + DPHI_NW * QW - 1) / (DPHI_NW * QW);
   const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
   if (nb_full * p.BH < 256 && nb_half > nb_full)
-    return launch_dphi_nw<KIND, NPAIR, HW>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
+    return launch_dphi_nw<KIND, NPAIR, DPHI_NW, 1>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
   return launch_dphi_nw<KIND, NPAIR, DPHI_NW>(p, X, ofrag, prep, Wv, wz, DX, keys, s);
 }
 
