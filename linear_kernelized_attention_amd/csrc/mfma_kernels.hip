@@ -504,12 +504,13 @@ void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, lo
     launch_readout_nw<KIND, RO_NW, NPAIR, MODE, 2>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
     return;
   }
-  // The trig forward with at most 8 Omega row pairs: 16 waves of 32 queries
+  // The trig map with at most 8 Omega row pairs: 16 waves of 32 queries
   // (the same 512 queries per block, four waves per SIMD at 128 VGPRs, and
   // twice the loads in flight in the prologue): headline readout 22.7 ->
-  // 21.9 us, B1 H8 L32768 38.3 -> 36.6 us.  The positive map measured
+  // 21.9 us, B1 H8 L32768 38.3 -> 36.6 us; the backward's two readouts
+  // (headline backward 152.9 -> 149.9 us).  The positive map measured
   // 16.8 -> 17.1 us this way and keeps 8 waves of 64.
-  if constexpr (MODE == RO_OUT && KIND == KIND_TRIG && NPAIR <= 8) {
+  if constexpr (KIND == KIND_TRIG && NPAIR <= 8) {
     launch_readout_nw<KIND, 2 * RO_NW, NPAIR, MODE, 2>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
     return;
   }
