@@ -271,6 +271,18 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
   };
 
   uint16_t* kt = (uint16_t*)Red[w];   // this wave's transposed phi(K) fragments
+  // Fragment `tile`, lane row: 16-byte rows, for the trig forward with a
+  // 16-byte gap after every 16 rows.  The transposing writes (lane
+  // 16 g' + c -> row 16 (c / 4) + 4 g' + r, word c % 4) then reach 64
+  // distinct banks instead of 16 (rows 16 apart fall on the same banks
+  // without the gap), and the fragment reads stay 16 contiguous bytes per
+  // lane: c3 chunk kernel 53.0 -> 51.8 us.  The other maps and the
+  // backward modes measured slower with it (positive map 43.6 -> 46.1 us,
+  // causal backward 291.6 -> 295.0 us) and keep the plain rows.
+  constexpr bool KT_PAD = TRIG && MODE == C_OUT;
+  auto kt_off = [](int tile, int row) {
+    return KT_PAD ? (tile * 68 + row + (row >> 4)) * 8 : (tile * 64 + row) * 8;
+  };
 
   auto compute = [&](int buf) {
     const uint16_t* qs = Qs[buf];
@@ -319,8 +331,8 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
       for (int j = 0; j < 8; ++j) {
         const int ts = j >> 2, r = j & 3;
         const int dl = 16 * (c >> 2) + 4 * g + r, ds = 2 * (c & 3);
-        *(uint32_t*)&kt[((ts * KS + 0) * 64 + dl) * 8 + ds] = pack2(sv[0][j], sv[1][j]);
-        if (TRIG) *(uint32_t*)&kt[((ts * KS + 1) * 64 + dl) * 8 + ds] = pack2(cv[0][j], cv[1][j]);
+        *(uint32_t*)&kt[kt_off(ts * KS + 0, dl) + ds] = pack2(sv[0][j], sv[1][j]);
+        if (TRIG) *(uint32_t*)&kt[kt_off(ts * KS + 1, dl) + ds] = pack2(cv[0][j], cv[1][j]);
       }
     }
     // (d) query projection P_Q^T[ot][nt]: Omega row 16 ot + 4 g + r, token 16 nt + c
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(NW * 64) void causal_kernel(
     for (int mk = 0; mk < 2; ++mk) {
       bf16x8 ka[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ka[s] = *(const bf16x8*)&kt[((mk * KS + s) * 64 + lane) * 8];
+      for (int s = 0; s < KS; ++s) ka[s] = *(const bf16x8*)&kt[kt_off(mk * KS + s, lane)];
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         floatx4 p = {0.f, 0.f, 0.f, 0.f};
