@@ -180,3 +180,21 @@ def test_autograd_function(dtype, causal, kind):
             den = nr if nr > 1e-6 * np.linalg.norm(sc[i]) else np.linalg.norm(sc[i])
             e = max(e, np.linalg.norm(got[i] - rr[i]) / den)
         assert e <= TOL[dtype], (name, e)
+
+
+def test_forward_den_full_grid_trig():
+    # the headline shape, where the trig readout runs 16 waves of 32 queries
+    # per block: its row normalisers (the query rows reloaded in the
+    # epilogue) against the oracle's feature maps, and the output unchanged
+    # by asking for them
+    B, H, L, d, m, dtype = 4, 8, 4096, 64, 256, "bf16"
+    assert F.favor_attention_resolve_path(B, H, L, d, m, dtype, "trig", False) == "mfma"
+    dev, (q, k, v), W = problem(B, H, L, d, m, dtype, seed=8)
+    ref = _oracle_den(q, k, W, "trig", False)
+    out, den = F.favor_attention(*dev, kind="trig", causal=False, path="mfma", den=True)
+    plain = F.favor_attention(*dev, kind="trig", causal=False, path="mfma")
+    torch.cuda.synchronize()
+    err = _rel(den.cpu().numpy().astype(np.float64), ref)
+    print(f"[mfma] B4 H8 L4096 trig den rel = {err:.2e}", flush=True)
+    assert err <= TOL[dtype], err
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
