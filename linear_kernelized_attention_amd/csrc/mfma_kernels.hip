@@ -501,6 +501,13 @@ void launch_readout(const Problem& p, const Buffers& b, const uint16_t* part, lo
   const long long nb_full = (p.L + RO_NW * QW - 1) / (RO_NW * QW);
   const long long nb_half = (p.L + HW * QW - 1) / (HW * QW);
   if (nb_full * p.BH < 256 && nb_half > nb_full) {
+    // the backward's readouts: 16 waves of one query tile each (B8 H8 L1024
+    // trig backward 104.8 -> 101.8 us); the forward measured slower so
+    // (readout 12.4 -> 13.7 us trig, 9.7 -> 11.3 us ReLU)
+    if constexpr (MODE != RO_OUT && NPAIR <= 8) {
+      launch_readout_nw<KIND, 2 * RO_NW, NPAIR, MODE, 1>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
+      return;
+    }
     launch_readout_nw<KIND, RO_NW, NPAIR, MODE, 2>(p, b, part, split_stride, nsum, ofrag, s, G, bhat);
     return;
   }
